@@ -1,0 +1,147 @@
+"""Reference model of the block-pool allocator -- TEST INFRASTRUCTURE ONLY (pure Python).
+
+Follows the pages' statement of the problem:
+  * one pool of fixed-size physical blocks; any free block serves any request
+    ("vLLM and PagedAttention" slides, slide 12, and the "Week 22 Day 2"
+    lesson note, section 2: any free block can satisfy any request);
+  * a per-sequence block table maps logical block j (tokens j*B .. j*B+B-1) to
+    a physical block (slide 10; lesson note section 2, block-table diagram);
+  * a new block is taken only when the last one is full (slide 11);
+  * sharing increments a block's reference count (lesson note section 3.1);
+  * a sequence about to write into a shared, partly filled last block gets a
+    private copy first; only the last block is ever copied (slide 13, lesson
+    note section 3.2);
+  * finished sequences return their blocks at once (lesson note section 4);
+  * a request that cannot get all its blocks gets none (slide 15).
+
+Readings where the pages fix no detail (the GPU library's allocator makes the
+same choices independently):
+  * free blocks form a LIFO stack; ``free_order[0]`` is handed out first;
+  * a freed sequence returns its blocks in logical order, so its last block is
+    the next one handed out;
+  * within one batched append, sequences are served in the order given, and
+    the whole batch fails, changing nothing, if the pool runs short.
+"""
+from __future__ import annotations
+
+import copy
+
+
+class OutOfBlocks(Exception):
+    pass
+
+
+class BlockPool:
+    def __init__(self, num_blocks, block_size, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = order[::-1]  # top of the stack is the end of the list
+        self.ref = [0] * num_blocks
+        self.seqs = {}  # sid -> [blocks(list), length(int)]
+
+    # -- queries ---------------------------------------------------------
+    def num_free(self):
+        return len(self.free)
+
+    def length(self, sid):
+        return self.seqs[sid][1]
+
+    def blocks(self, sid):
+        return list(self.seqs[sid][0])
+
+    # -- lifecycle -------------------------------------------------------
+    def add(self, sid):
+        if sid in self.seqs:
+            raise KeyError(f"sequence {sid} exists")
+        self.seqs[sid] = [[], 0]
+
+    def fork(self, parent, child):
+        if child in self.seqs:
+            raise KeyError(f"sequence {child} exists")
+        blocks, n = self.seqs[parent]
+        for b in blocks:
+            self.ref[b] += 1
+        self.seqs[child] = [list(blocks), n]
+
+    def free_seq(self, sid):
+        blocks, _ = self.seqs.pop(sid)
+        for b in blocks:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    def _take(self):
+        b = self.free.pop()
+        self.ref[b] = 1
+        return b
+
+    def _append_one(self, sid, n):
+        B = self.block_size
+        blocks, length = self.seqs[sid]
+        pairs = []
+        if n == 0:
+            return [], pairs
+        if length % B and self.ref[blocks[-1]] > 1:
+            if not self.free:
+                raise OutOfBlocks()
+            old = blocks[-1]
+            new = self._take()
+            self.ref[old] -= 1
+            blocks[-1] = new
+            pairs.append((old, new))
+        while len(blocks) * B < length + n:
+            if not self.free:
+                raise OutOfBlocks()
+            blocks.append(self._take())
+        slots = [blocks[t // B] * B + t % B for t in range(length, length + n)]
+        self.seqs[sid][1] = length + n
+        return slots, pairs
+
+    def append(self, requests):
+        """requests: [(sid, n_tokens), ...]. Returns (slots, copy pairs); all or nothing."""
+        sids = [s for s, _ in requests]
+        if len(set(sids)) != len(sids):
+            raise ValueError("a sequence appears twice in one batch")
+        for s in sids:
+            if s not in self.seqs:
+                raise KeyError(f"unknown sequence {s}")
+        saved = (list(self.free), list(self.ref), copy.deepcopy(self.seqs))
+        slots, pairs = [], []
+        try:
+            for sid, n in requests:
+                sl, pr = self._append_one(sid, int(n))
+                slots += sl
+                pairs += pr
+        except OutOfBlocks:
+            self.free, self.ref, self.seqs = saved
+            raise
+        return slots, pairs
+
+    def tables(self, sids, max_blocks, pad=-1):
+        rows, ctx = [], []
+        for s in sids:
+            blocks, n = self.seqs[s]
+            if len(blocks) > max_blocks:
+                raise ValueError("max_blocks too small")
+            rows.append(list(blocks) + [pad] * (max_blocks - len(blocks)))
+            ctx.append(n)
+        return rows, ctx
+
+    def check_invariants(self):
+        """One pool; reference counts count sharers; a block is free iff its count is zero."""
+        N = self.num_blocks
+        assert len(set(self.free)) == len(self.free)
+        used = {b for blocks, _ in self.seqs.values() for b in blocks}
+        assert len(self.free) + len(used) == N
+        for b in range(N):
+            holders = sum(blocks.count(b) for blocks, _ in self.seqs.values())
+            assert self.ref[b] == holders, (b, self.ref[b], holders)
+            assert (b in self.free) == (holders == 0)
+        B = self.block_size
+        for blocks, n in self.seqs.values():
+            assert len(blocks) == -(-n // B)
