@@ -1,0 +1,198 @@
+/*
+ * pkv -- paged key/value cache and decode attention for AMD MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only. Host pointers are marked (host);
+ * every other pointer is device memory that the CALLER allocates and owns:
+ * the library never allocates, frees or retains device memory.
+ *
+ * Cache layout (both K and V): [num_blocks][num_kv_heads][block_size][head_dim],
+ * row-major, head_dim innermost. Token t of a sequence lives in physical block
+ * table[t / block_size], row t % block_size; its slot number is
+ * physical_block * block_size + t % block_size.
+ *
+ * Sources: "vLLM and PagedAttention: Virtual Memory for LLM Serving" (slides 9-16)
+ * and "Week 22 Day 2: High-Throughput Serving with vLLM & PagedAttention"
+ * (sections 2-4), which state the problem: fixed-size blocks reached through a
+ * per-sequence block table, one shared pool, allocation only when the last block
+ * fills, reference-counted sharing with copy-on-write of the last block, and
+ * attention computed block by block from non-contiguous blocks.
+ *
+ * Errors: every int-returning call returns a pkv_status. On failure nothing is
+ * launched and no state changes; pkv_last_error() describes the failure
+ * (thread-local, valid until the next call on the same thread).
+ * Kernel calls enqueue on the given stream and return without waiting; only
+ * launch-time errors are reported synchronously.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef PKV_HIP_STREAM_DEFINED
+#define PKV_HIP_STREAM_DEFINED
+typedef struct ihipStream_t *hipStream_t; /* same declaration as <hip/hip_runtime_api.h> */
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_EINVAL = -1,      /* bad argument; nothing launched, nothing changed */
+    PKV_ENOMEM = -2,      /* block pool exhausted; pool state unchanged */
+    PKV_ENOSEQ = -3,      /* unknown sequence id */
+    PKV_EHIP = -4,        /* HIP runtime / launch error */
+    PKV_EUNSUPPORTED = -5,/* dtype / head_dim / block_size / group combination not built */
+    PKV_EEXIST = -6       /* sequence id already in use */
+} pkv_status;
+
+typedef enum pkv_dtype {
+    PKV_F32 = 0,
+    PKV_F16 = 1,  /* IEEE binary16 */
+    PKV_BF16 = 2  /* bfloat16 */
+} pkv_dtype;
+
+/* Attention flags. */
+#define PKV_FLAG_SCALAR_GQA 1u /* use the one-query-head-per-workgroup kernel even when G > 1 */
+
+const char *pkv_last_error(void);
+const char *pkv_version(void);
+
+/* ======================================================================
+ * Host block-pool allocator (the scheduler side; slides 10-16).
+ * A pool is host-only state owned by one scheduler thread; not thread-safe.
+ * ==================================================================== */
+typedef struct pkv_pool pkv_pool;
+
+/* One pool of num_blocks physical blocks of block_size tokens ("one pool instead
+ * of private reserves", slide 12). free_order (host, nullable) is a permutation of
+ * 0..num_blocks-1: the order in which free blocks are handed out (NULL = ascending).
+ * Free blocks form a LIFO stack: a freed block is the next one handed out. */
+int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order, pkv_pool **out);
+void pkv_pool_destroy(pkv_pool *pool);
+int32_t pkv_pool_num_blocks(const pkv_pool *pool);
+int32_t pkv_pool_block_size(const pkv_pool *pool);
+int32_t pkv_pool_num_free(const pkv_pool *pool);
+/* Reference count of a physical block (number of sequences mapping it); -1 if out of range. */
+int32_t pkv_block_ref_count(const pkv_pool *pool, int32_t block);
+
+/* A new, empty sequence. PKV_EEXIST if seq_id is in use. */
+int pkv_seq_add(pkv_pool *pool, int64_t seq_id);
+/* Drop a sequence: every block's count is decremented; blocks reaching zero return to
+ * the pool at once, in logical order (lesson note, section 4: finished sequences free
+ * their blocks immediately). */
+int pkv_seq_free(pkv_pool *pool, int64_t seq_id);
+/* child shares all of parent's blocks: same table and length, every block's count + 1
+ * (slide 14; lesson note section 3: ref_count <- ref_count + 1). */
+int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t child);
+/* Length in tokens (>= 0), or PKV_ENOSEQ. */
+int64_t pkv_seq_len(const pkv_pool *pool, int64_t seq_id);
+/* Number of blocks of the sequence (>= 0), or PKV_ENOSEQ. */
+int32_t pkv_seq_num_blocks(const pkv_pool *pool, int64_t seq_id);
+/* Copy the sequence's block table (host out[cap]); returns the number of blocks or an error. */
+int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32_t cap);
+
+/* Reserve n_tokens[i] new token slots at the end of each sequence seq_ids[i] (host arrays),
+ * for all n_seqs sequences together: either every sequence gets its slots or, with
+ * PKV_ENOMEM, none does and nothing changes (slide 15: all-or-nothing).
+ *  - A block is taken only when the last one is full (slide 11).
+ *  - If a sequence's last block is shared (count > 1) and partly filled, the sequence
+ *    first gets a private copy: a new block dst, the pair (src, dst) is emitted, src's
+ *    count drops by one (slide 13: only the last block is ever copied). The last sharer
+ *    left writes in place, so n sharers make n-1 copies.
+ * Sequences are served in the order given; a sequence may appear once per call.
+ * slots_out (host, int64[sum n_tokens]) receives the slots in request order;
+ * cow_pairs_out (host, int32[2*max_pairs]) receives (src, dst) pairs, their count in
+ * *n_pairs_out. More pairs than max_pairs: PKV_EINVAL, nothing changes.
+ * The caller must run pkv_copy_blocks on the pairs before pkv_reshape_and_cache writes
+ * the new tokens (same stream). */
+int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_tokens, int32_t n_seqs,
+                   int64_t *slots_out, int32_t *cow_pairs_out, int32_t max_pairs, int32_t *n_pairs_out);
+
+/* Block tables of n sequences as a dense host array tables_out[n][max_blocks] (row i for
+ * seq_ids[i]), padded with pad_value past each sequence's blocks, and their lengths in
+ * ctx_out[n] (host). A sequence with more than max_blocks blocks: PKV_EINVAL.
+ * The caller uploads both to the device every step (slide 16: workers receive the
+ * block tables with every step). */
+int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t max_blocks,
+                           int32_t pad_value, int32_t *tables_out, int32_t *ctx_out);
+
+/* ======================================================================
+ * Device kernels. dtype is a pkv_dtype; all tensors of one call share it.
+ * ==================================================================== */
+
+/* Write new tokens' keys and values into their slots (slide 11: a new token goes into
+ * the free slot of the last block).
+ *  key, value:   [num_tokens][num_kv_heads][head_dim], token rows key_stride / value_stride
+ *                elements apart (>= num_kv_heads*head_dim; lets K and V be views of a
+ *                fused projection output).
+ *  k_cache, v_cache: the caches, num_blocks blocks each.
+ *  slot_mapping: device int64[num_tokens]; a negative slot is skipped (padding).
+ * Byte-exact copy. Slots >= num_blocks*block_size are skipped by the kernel (a caller
+ * error). Duplicate non-negative slots in one call are a caller error (result
+ * unspecified). Pointers must be 16-byte aligned and strides*elt multiples of 16. */
+int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride, int64_t value_stride,
+                          void *k_cache, void *v_cache, int64_t num_blocks, const int64_t *slot_mapping,
+                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t dtype, hipStream_t stream);
+
+/* Copy whole blocks for copy-on-write (slide 13): for each pair p, block pairs[2p+1]
+ * becomes a byte copy of block pairs[2p], in the K and the V cache of every layer.
+ *  k_caches, v_caches: host arrays of num_layers device pointers.
+ *  pairs: host int32[2*num_pairs] (src, dst), e.g. straight from pkv_seq_append.
+ *  block_bytes: bytes of one block of one cache (num_kv_heads*block_size*head_dim*elt).
+ * Checked on the host: every block in [0, num_blocks), dst values distinct, no dst equal
+ * to any src (so the order of copies cannot matter); otherwise PKV_EINVAL. */
+int pkv_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers, int64_t num_blocks,
+                    int64_t block_bytes, const int32_t *pairs, int32_t num_pairs, hipStream_t stream);
+
+/* Bytes of fp32 workspace the split-partition mode needs:
+ * num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4.
+ * 0 when partition_size == 0. */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_size);
+
+/* Decode attention over the paged cache, one query token per sequence (slide 9: attention
+ * block by block; keys and values fetched from non-contiguous blocks by address):
+ *   for each sequence s and query head h (kv head h / (num_q_heads/num_kv_heads)):
+ *   out[s][h] = softmax_t(scale * q[s][h] . K_t) . V_t over t < context_lens[s],
+ *   K_t, V_t read from block block_tables[s][t / block_size], row t % block_size.
+ *  out, q:        [num_seqs][num_q_heads][head_dim]; out is written in dtype (RNE).
+ *  block_tables:  device int32[num_seqs][max_blocks_per_seq]; entries past a sequence's
+ *                 last block are never read.
+ *  context_lens:  device int32[num_seqs]; a sequence with length 0 gets zeros.
+ *  max_context_len: host bound on context_lens, sizes the launch.
+ *  partition_size: 0 = one pass per (sequence, head). > 0 (a multiple of block_size):
+ *                 each (sequence, head) is cut into parts of that many tokens, computed
+ *                 independently into workspace, then merged by a log-sum-exp reduce pass.
+ *  workspace:     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned;
+ *                 may be NULL when partition_size == 0.
+ *  flags:         PKV_FLAG_SCALAR_GQA or 0.
+ * Device-side guards (never faults on bad tables, but the result is then unspecified):
+ * lengths are clamped to [0, min(max_context_len, max_blocks_per_seq*block_size)] and a
+ * table entry outside [0, num_blocks) contributes no tokens.
+ * Supported: dtype f32/f16/bf16; head_dim 64 or 128; block_size 8, 16 or 32;
+ * num_q_heads a multiple of num_kv_heads. */
+int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                               int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                               const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                               int32_t dtype, uint32_t flags, hipStream_t stream);
+
+/* The same attention over a contiguous cache, the layout paging replaces (slide 19 prices
+ * the indirection against it): k, v are [num_seqs][num_kv_heads][lmax][head_dim] and token t
+ * of (s, kv head) is row t of that slab. Same kernels, same tiling; only the address of a
+ * tile differs. Lengths are clamped to [0, min(max_context_len, lmax)]. */
+int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, const void *v, int32_t lmax,
+                                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
+                                    int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                    int32_t dtype, uint32_t flags, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -170,13 +170,15 @@ def batch_tables(pool, batch, pad=-1):
     return np.array(rows, dtype=np.int32).reshape(len(batch), mb), np.array(ctx, dtype=np.int32)
 
 
-def replay(w, attend_checks=True, partition_size=None):
-    """Run a workload's operations with the oracle's allocator model, scatter and copy."""
+def replay(w, attend_checks=True, partition_size=None, after_op=None):
+    """Run a workload's operations with the oracle's allocator model, scatter and copy.
+
+    after_op(index, op, state), if given, is called after each operation."""
     pool = BlockPool(w.num_blocks, w.block_size, w.free_order)
     kc = poisoned_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.dtype)
     vc = poisoned_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, w.dtype)
     st = OracleState(pool=pool, k_cache=kc, v_cache=vc)
-    for op in w.ops:
+    for i, op in enumerate(w.ops):
         kind = op[0]
         if kind == "add":
             pool.add(op[1])
@@ -201,6 +203,8 @@ def replay(w, attend_checks=True, partition_size=None):
                                                  w.partition_size if partition_size is None else partition_size))
         else:
             raise ValueError(kind)
+        if after_op is not None:
+            after_op(i, op, st)
     return st
 
 

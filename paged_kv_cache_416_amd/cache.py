@@ -1,0 +1,116 @@
+"""PagedKVCache: the native block pool plus one layer's device K/V caches, driven step by step.
+
+Mirrors the pages' split of roles ("vLLM and PagedAttention" slide 16): the host side
+owns the block tables and assigns slots; each step it ships slot numbers and tables to
+the device, where copy_blocks, reshape_and_cache and the attention kernel run on one stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import kernels
+from .pool import Pool
+
+_POISON_BITS = {torch.float32: 0x7FC00000, torch.float16: 0x7E00, torch.bfloat16: 0x7FC0}
+_INT_VIEW = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+
+
+def poison_(t: torch.Tensor) -> torch.Tensor:
+    """Fill a float tensor with quiet NaNs (a fill kernel, no memset), so stray reads show up."""
+    t.view(_INT_VIEW[t.dtype]).fill_(_POISON_BITS[t.dtype])
+    return t
+
+
+class PagedKVCache:
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, dtype, device=None, free_order=None,
+                 poison=True):
+        self.device = torch.device(device or "cuda")
+        self.pool = Pool(num_blocks, block_size, free_order)
+        self.block_size = block_size
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.dtype = dtype
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        self.k = torch.empty(shape, dtype=dtype, device=self.device)
+        self.v = torch.empty(shape, dtype=dtype, device=self.device)
+        if poison:
+            poison_(self.k)
+            poison_(self.v)
+        self.last_slots = None
+        self.last_pairs = None
+
+    # -- scheduler side -------------------------------------------------
+    def add(self, sid):
+        self.pool.add(sid)
+
+    def fork(self, parent, child):
+        self.pool.fork(parent, child)
+
+    def free(self, sid):
+        self.pool.free(sid)
+
+    def append(self, sids, keys, values):
+        """Append keys[i]/values[i] ([n_i, Hkv, D] device tensors) to sequence sids[i], all or nothing.
+
+        Runs copy-on-write copies first, then writes every new token into its slot, on one stream.
+        """
+        reqs = [(int(s), int(k.shape[0])) for s, k in zip(sids, keys)]
+        slots, pairs = self.pool.append(reqs)
+        self.last_slots, self.last_pairs = slots, pairs
+        if len(pairs):
+            kernels.copy_blocks([self.k], [self.v], pairs)
+        if len(slots):
+            key = torch.cat(list(keys)) if len(keys) > 1 else keys[0]
+            val = torch.cat(list(values)) if len(values) > 1 else values[0]
+            sm = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device)
+            kernels.reshape_and_cache(key, val, self.k, self.v, sm)
+        return slots, pairs
+
+    def tables(self, sids, pad=-1):
+        """Device block tables, device lengths and the host bound on the lengths."""
+        tb, ctx = self.pool.tables(sids, pad=pad)
+        return (torch.from_numpy(tb).to(self.device), torch.from_numpy(ctx).to(self.device),
+                int(ctx.max(initial=0)))
+
+    # -- device side ----------------------------------------------------
+    def attention(self, q, sids, scale, partition_size=0, flags=0, out=None):
+        tb, ctx, mx = self.tables(sids)
+        out = torch.empty_like(q) if out is None else out
+        ws = kernels.alloc_workspace(q.shape[0], q.shape[1], q.shape[2], mx, partition_size, self.device)
+        return kernels.paged_attention_decode(out, q, self.k, self.v, tb, ctx, mx, scale, partition_size, ws, flags)
+
+
+def to_device(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
+    """Upload a storage array (float32 / float16 / uint16 bf16 bits) as a tensor of `dtype`."""
+    if dtype == torch.bfloat16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def run_ops(cache: PagedKVCache, ops, dtype, on_check=None):
+    """Replay a list of scheduler operations:
+    ("add", sid) | ("fork", parent, child) | ("free", sid) | ("append", [(sid, k, v), ...]) | ("check",).
+    k, v are host storage arrays [n, Hkv, D]. on_check() is called at each ("check",)."""
+    for op in ops:
+        kind = op[0]
+        if kind == "add":
+            cache.add(op[1])
+        elif kind == "fork":
+            cache.fork(op[1], op[2])
+        elif kind == "free":
+            cache.free(op[1])
+        elif kind == "append":
+            sids = [sid for sid, _, _ in op[1]]
+            keys = to_device(np.concatenate([k for _, k, _ in op[1]]), dtype, cache.device)
+            vals = to_device(np.concatenate([v for _, _, v in op[1]]), dtype, cache.device)
+            # one launch per step: split back into per-sequence views only for the row counts
+            counts = [k.shape[0] for _, k, _ in op[1]]
+            ks = list(torch.split(keys, counts))
+            vs = list(torch.split(vals, counts))
+            cache.append(sids, ks, vs)
+        elif kind == "check":
+            if on_check is not None:
+                on_check()
+        else:
+            raise ValueError(f"unknown op {kind}")

@@ -1,0 +1,147 @@
+// Cache writes (reshape_and_cache) and copy-on-write block copies (copy_blocks).
+//
+// Both are byte moves: every thread moves 16-byte chunks with one vector load
+// and one vector store, consecutive threads on consecutive chunks, so a wave
+// touches 1 KiB of contiguous memory per instruction on each side.
+#include "common.h"
+
+namespace pkv {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// One thread per 16-byte chunk of one (token, kv head) row, grid-stride.
+// Token i, head h goes to block slot/B, row slot%B of head h (slide 11: a new
+// token goes into the free slot of the sequence's last block).
+__global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
+    const char *__restrict__ key, const char *__restrict__ value, int64_t key_stride_b, int64_t value_stride_b,
+    char *__restrict__ k_cache, char *__restrict__ v_cache, int64_t num_slots, const int64_t *__restrict__ slots,
+    int64_t total_chunks, int32_t chunks_per_row, int32_t num_kv_heads, int32_t block_size) {
+    const int32_t row_bytes = chunks_per_row * 16;
+    const int64_t per_token = static_cast<int64_t>(chunks_per_row) * num_kv_heads;
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total_chunks;
+         i += static_cast<int64_t>(gridDim.x) * kThreads) {
+        const int64_t token = i / per_token;
+        const int32_t rem = static_cast<int32_t>(i - token * per_token);
+        const int32_t h = rem / chunks_per_row;
+        const int32_t c = rem - h * chunks_per_row;
+        const int64_t slot = slots[token];
+        if (slot < 0 || slot >= num_slots) continue;  // padding, or a slot outside the pool
+        const int64_t blk = slot / block_size;
+        const int64_t off = slot - blk * block_size;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + c * 16;
+        const u32x4 kv = *reinterpret_cast<const u32x4 *>(key + token * key_stride_b + h * row_bytes + c * 16);
+        const u32x4 vv = *reinterpret_cast<const u32x4 *>(value + token * value_stride_b + h * row_bytes + c * 16);
+        *reinterpret_cast<u32x4 *>(k_cache + dst) = kv;
+        *reinterpret_cast<u32x4 *>(v_cache + dst) = vv;
+    }
+}
+
+constexpr int kMaxLayers = 16;
+constexpr int kMaxPairs = 64;
+
+struct CopyArgs {
+    char *cache[2 * kMaxLayers];  // K of layer l at 2l, V at 2l+1
+    int32_t src[kMaxPairs];
+    int32_t dst[kMaxPairs];
+    int64_t block_bytes;
+};
+
+// grid = (slices, pairs, 2 * layers): workgroup (x, p, c) copies slice x of pair p in cache c.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const CopyArgs a) {
+    char *base = a.cache[blockIdx.z];
+    const char *src = base + a.src[blockIdx.y] * a.block_bytes;
+    char *dst = base + a.dst[blockIdx.y] * a.block_bytes;
+    for (int64_t off = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 16; off < a.block_bytes;
+         off += static_cast<int64_t>(gridDim.x) * kThreads * 16)
+        *reinterpret_cast<u32x4 *>(dst + off) = *reinterpret_cast<const u32x4 *>(src + off);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride, int64_t value_stride,
+                                     void *k_cache, void *v_cache, int64_t num_blocks, const int64_t *slot_mapping,
+                                     int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t dtype, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return fail(PKV_EINVAL, "pkv_reshape_and_cache: bad dtype %d", dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PKV_EINVAL, "pkv_reshape_and_cache: bad sizes");
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+        return fail(PKV_EINVAL, "pkv_reshape_and_cache: NULL pointer");
+    const int eb = elt_bytes(dtype);
+    const int64_t row_bytes = static_cast<int64_t>(head_dim) * eb;
+    if (row_bytes % 16) return fail(PKV_EINVAL, "pkv_reshape_and_cache: head_dim*elt must be a multiple of 16 bytes");
+    if (key_stride < static_cast<int64_t>(num_kv_heads) * head_dim ||
+        value_stride < static_cast<int64_t>(num_kv_heads) * head_dim)
+        return fail(PKV_EINVAL, "pkv_reshape_and_cache: token stride smaller than num_kv_heads*head_dim");
+    if ((key_stride * eb) % 16 || (value_stride * eb) % 16 || !aligned16(key) || !aligned16(value) ||
+        !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PKV_EINVAL, "pkv_reshape_and_cache: pointers and strides must be 16-byte aligned");
+    const int32_t cpr = static_cast<int32_t>(row_bytes / 16);
+    const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * cpr;
+    const int64_t want = ceil_div(total, kThreads);
+    const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<const char *>(key), static_cast<const char *>(value), key_stride * eb,
+                       value_stride * eb, static_cast<char *>(k_cache), static_cast<char *>(v_cache),
+                       num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size);
+    return hip_status(hipGetLastError(), "pkv_reshape_and_cache launch");
+}
+
+extern "C" int pkv_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers, int64_t num_blocks,
+                               int64_t block_bytes, const int32_t *pairs, int32_t num_pairs, hipStream_t stream) {
+    if (num_pairs < 0 || num_layers < 0 || num_blocks <= 0 || block_bytes <= 0)
+        return fail(PKV_EINVAL, "pkv_copy_blocks: bad sizes");
+    if (num_pairs == 0 || num_layers == 0) return PKV_OK;
+    if (!k_caches || !v_caches || !pairs) return fail(PKV_EINVAL, "pkv_copy_blocks: NULL pointer");
+    if (block_bytes % 16) return fail(PKV_EINVAL, "pkv_copy_blocks: block_bytes must be a multiple of 16");
+    for (int32_t l = 0; l < num_layers; ++l)
+        if (!k_caches[l] || !v_caches[l] || !aligned16(k_caches[l]) || !aligned16(v_caches[l]))
+            return fail(PKV_EINVAL, "pkv_copy_blocks: layer %d cache pointer NULL or not 16-byte aligned", l);
+    // Host check: in range, distinct destinations, no destination is also a source. Then
+    // the copies are independent and may run in any order.
+    {
+        std::vector<char> is_src(num_blocks, 0), is_dst(num_blocks, 0);
+        for (int32_t p = 0; p < num_pairs; ++p) {
+            const int32_t s = pairs[2 * p], d = pairs[2 * p + 1];
+            if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+                return fail(PKV_EINVAL, "pkv_copy_blocks: pair %d (%d, %d) outside [0, %lld)", p, s, d,
+                            (long long)num_blocks);
+            if (is_dst[d]) return fail(PKV_EINVAL, "pkv_copy_blocks: block %d is a destination twice", d);
+            is_dst[d] = 1;
+            is_src[s] = 1;
+        }
+        for (int32_t p = 0; p < num_pairs; ++p)
+            if (is_src[pairs[2 * p + 1]])
+                return fail(PKV_EINVAL, "pkv_copy_blocks: block %d is both a source and a destination",
+                            pairs[2 * p + 1]);
+    }
+    const int64_t per_wg = static_cast<int64_t>(kThreads) * 16 * 4;  // ~16 KiB per workgroup
+    const unsigned slices = static_cast<unsigned>(std::min<int64_t>(ceil_div(block_bytes, per_wg), 64));
+    for (int32_t l0 = 0; l0 < num_layers; l0 += kMaxLayers) {
+        const int32_t nl = std::min(kMaxLayers, num_layers - l0);
+        for (int32_t p0 = 0; p0 < num_pairs; p0 += kMaxPairs) {
+            const int32_t np = std::min(kMaxPairs, num_pairs - p0);
+            CopyArgs a{};
+            for (int32_t l = 0; l < nl; ++l) {
+                a.cache[2 * l] = static_cast<char *>(k_caches[l0 + l]);
+                a.cache[2 * l + 1] = static_cast<char *>(v_caches[l0 + l]);
+            }
+            for (int32_t p = 0; p < np; ++p) {
+                a.src[p] = pairs[2 * (p0 + p)];
+                a.dst[p] = pairs[2 * (p0 + p) + 1];
+            }
+            a.block_bytes = block_bytes;
+            hipLaunchKernelGGL(copy_blocks_kernel, dim3(slices, np, 2 * nl), dim3(kThreads), 0, stream, a);
+            int rc = hip_status(hipGetLastError(), "pkv_copy_blocks launch");
+            if (rc) return rc;
+        }
+    }
+    return PKV_OK;
+}

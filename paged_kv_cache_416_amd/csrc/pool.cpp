@@ -1,0 +1,232 @@
+// Host block-pool allocator: the scheduler-side half of the paged KV cache.
+//
+// "vLLM and PagedAttention" slides 10-16 and the "Week 22 Day 2" lesson note,
+// sections 2-4: one pool of fixed-size blocks shared by all requests, a
+// per-sequence block table, a new block only when the last one is full,
+// reference-counted sharing (fork), copy-on-write of a shared, partly filled
+// last block, immediate release of a finished sequence's blocks, and
+// all-or-nothing admission when the pool runs short.
+//
+// Choices the pages leave open: free blocks form a LIFO stack (free_order[0]
+// is handed out first; a freed block is the next one handed out); a freed
+// sequence returns its blocks in logical order; a batched append serves its
+// sequences in the order given.
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "common.h"
+
+using pkv::fail;
+
+struct pkv_pool {
+    struct Seq {
+        std::vector<int32_t> blocks;  // logical block j -> physical block
+        int64_t len = 0;              // tokens written
+    };
+    int32_t num_blocks = 0;
+    int32_t block_size = 0;
+    std::vector<int32_t> free_stack;  // back() is handed out next
+    std::vector<int32_t> ref;         // sequences mapping each block
+    std::unordered_map<int64_t, Seq> seqs;
+
+    int32_t take() {
+        int32_t b = free_stack.back();
+        free_stack.pop_back();
+        ref[b] = 1;
+        return b;
+    }
+};
+
+extern "C" {
+
+int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order, pkv_pool **out) {
+    if (!out) return fail(PKV_EINVAL, "pkv_pool_create: out is NULL");
+    *out = nullptr;
+    if (num_blocks <= 0 || block_size <= 0)
+        return fail(PKV_EINVAL, "pkv_pool_create: num_blocks=%d block_size=%d must be positive", num_blocks,
+                    block_size);
+    auto *p = new pkv_pool;
+    p->num_blocks = num_blocks;
+    p->block_size = block_size;
+    p->ref.assign(num_blocks, 0);
+    p->free_stack.resize(num_blocks);
+    if (free_order) {
+        std::vector<char> seen(num_blocks, 0);
+        for (int32_t i = 0; i < num_blocks; ++i) {
+            int32_t b = free_order[i];
+            if (b < 0 || b >= num_blocks || seen[b]) {
+                delete p;
+                return fail(PKV_EINVAL, "pkv_pool_create: free_order is not a permutation (entry %d = %d)", i, b);
+            }
+            seen[b] = 1;
+            p->free_stack[num_blocks - 1 - i] = b;
+        }
+    } else {
+        for (int32_t i = 0; i < num_blocks; ++i) p->free_stack[num_blocks - 1 - i] = i;
+    }
+    *out = p;
+    return PKV_OK;
+}
+
+void pkv_pool_destroy(pkv_pool *pool) { delete pool; }
+
+int32_t pkv_pool_num_blocks(const pkv_pool *pool) { return pool ? pool->num_blocks : PKV_EINVAL; }
+int32_t pkv_pool_block_size(const pkv_pool *pool) { return pool ? pool->block_size : PKV_EINVAL; }
+int32_t pkv_pool_num_free(const pkv_pool *pool) {
+    return pool ? static_cast<int32_t>(pool->free_stack.size()) : PKV_EINVAL;
+}
+
+int32_t pkv_block_ref_count(const pkv_pool *pool, int32_t block) {
+    if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+    return pool->ref[block];
+}
+
+int pkv_seq_add(pkv_pool *pool, int64_t seq_id) {
+    if (!pool) return fail(PKV_EINVAL, "pkv_seq_add: pool is NULL");
+    if (pool->seqs.count(seq_id)) return fail(PKV_EEXIST, "pkv_seq_add: sequence %lld exists", (long long)seq_id);
+    pool->seqs.emplace(seq_id, pkv_pool::Seq{});
+    return PKV_OK;
+}
+
+int pkv_seq_free(pkv_pool *pool, int64_t seq_id) {
+    if (!pool) return fail(PKV_EINVAL, "pkv_seq_free: pool is NULL");
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end()) return fail(PKV_ENOSEQ, "pkv_seq_free: unknown sequence %lld", (long long)seq_id);
+    for (int32_t b : it->second.blocks)
+        if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
+    pool->seqs.erase(it);
+    return PKV_OK;
+}
+
+int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t child) {
+    if (!pool) return fail(PKV_EINVAL, "pkv_seq_fork: pool is NULL");
+    auto it = pool->seqs.find(parent);
+    if (it == pool->seqs.end()) return fail(PKV_ENOSEQ, "pkv_seq_fork: unknown parent %lld", (long long)parent);
+    if (pool->seqs.count(child)) return fail(PKV_EEXIST, "pkv_seq_fork: sequence %lld exists", (long long)child);
+    pkv_pool::Seq copy = it->second;
+    for (int32_t b : copy.blocks) ++pool->ref[b];
+    pool->seqs.emplace(child, std::move(copy));
+    return PKV_OK;
+}
+
+int64_t pkv_seq_len(const pkv_pool *pool, int64_t seq_id) {
+    if (!pool) return fail(PKV_EINVAL, "pkv_seq_len: pool is NULL");
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end()) return fail(PKV_ENOSEQ, "pkv_seq_len: unknown sequence %lld", (long long)seq_id);
+    return it->second.len;
+}
+
+int32_t pkv_seq_num_blocks(const pkv_pool *pool, int64_t seq_id) {
+    if (!pool) return fail(PKV_EINVAL, "pkv_seq_num_blocks: pool is NULL");
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end())
+        return fail(PKV_ENOSEQ, "pkv_seq_num_blocks: unknown sequence %lld", (long long)seq_id);
+    return static_cast<int32_t>(it->second.blocks.size());
+}
+
+int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32_t cap) {
+    if (!pool || (!out && cap > 0)) return fail(PKV_EINVAL, "pkv_seq_blocks: NULL argument");
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end()) return fail(PKV_ENOSEQ, "pkv_seq_blocks: unknown sequence %lld", (long long)seq_id);
+    const auto &b = it->second.blocks;
+    if (static_cast<int64_t>(b.size()) > cap)
+        return fail(PKV_EINVAL, "pkv_seq_blocks: %zu blocks, room for %d", b.size(), cap);
+    for (size_t j = 0; j < b.size(); ++j) out[j] = b[j];
+    return static_cast<int32_t>(b.size());
+}
+
+int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_tokens, int32_t n_seqs,
+                   int64_t *slots_out, int32_t *cow_pairs_out, int32_t max_pairs, int32_t *n_pairs_out) {
+    if (!pool || n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_tokens)) || max_pairs < 0 ||
+        (max_pairs > 0 && !cow_pairs_out))
+        return fail(PKV_EINVAL, "pkv_seq_append: bad arguments");
+    const int64_t B = pool->block_size;
+    // Validation and a dry run that counts the blocks the whole batch needs, so that a
+    // batch the pool cannot serve changes nothing (slide 15: all or nothing).
+    std::unordered_set<int64_t> seen;
+    std::unordered_map<int32_t, int32_t> pending_drop;  // shared last blocks given up earlier in this batch
+    int64_t need = 0, total_tokens = 0;
+    int32_t pairs = 0;
+    std::vector<pkv_pool::Seq *> seqv(n_seqs);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        auto it = pool->seqs.find(seq_ids[i]);
+        if (it == pool->seqs.end())
+            return fail(PKV_ENOSEQ, "pkv_seq_append: unknown sequence %lld", (long long)seq_ids[i]);
+        if (!seen.insert(seq_ids[i]).second)
+            return fail(PKV_EINVAL, "pkv_seq_append: sequence %lld appears twice", (long long)seq_ids[i]);
+        if (n_tokens[i] < 0) return fail(PKV_EINVAL, "pkv_seq_append: n_tokens[%d] = %d < 0", i, n_tokens[i]);
+        pkv_pool::Seq &q = it->second;
+        seqv[i] = &q;
+        const int64_t n = n_tokens[i];
+        if (n == 0) continue;
+        if (q.len % B) {
+            int32_t last = q.blocks.back();
+            if (pool->ref[last] - pending_drop[last] > 1) {
+                ++pending_drop[last];
+                ++need;
+                ++pairs;
+            }
+        }
+        const int64_t blocks_after = pkv::ceil_div(q.len + n, B);
+        if (blocks_after > INT32_MAX)
+            return fail(PKV_EINVAL, "pkv_seq_append: sequence %lld too long", (long long)seq_ids[i]);
+        need += blocks_after - static_cast<int64_t>(q.blocks.size());
+        total_tokens += n;
+    }
+    if (total_tokens > 0 && !slots_out) return fail(PKV_EINVAL, "pkv_seq_append: slots_out is NULL");
+    if (pairs > max_pairs)
+        return fail(PKV_EINVAL, "pkv_seq_append: %d copy-on-write pairs, room for %d", pairs, max_pairs);
+    if (need > static_cast<int64_t>(pool->free_stack.size()))
+        return fail(PKV_ENOMEM, "pkv_seq_append: batch needs %lld blocks, %zu free", (long long)need,
+                    pool->free_stack.size());
+    // Apply.
+    int64_t k = 0;
+    int32_t np = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+        pkv_pool::Seq &q = *seqv[i];
+        const int64_t n = n_tokens[i];
+        if (n == 0) continue;
+        if (q.len % B && pool->ref[q.blocks.back()] > 1) {
+            const int32_t src = q.blocks.back();
+            const int32_t dst = pool->take();
+            --pool->ref[src];
+            q.blocks.back() = dst;
+            cow_pairs_out[2 * np] = src;
+            cow_pairs_out[2 * np + 1] = dst;
+            ++np;
+        }
+        while (static_cast<int64_t>(q.blocks.size()) * B < q.len + n) q.blocks.push_back(pool->take());
+        for (int64_t t = q.len; t < q.len + n; ++t) slots_out[k++] = static_cast<int64_t>(q.blocks[t / B]) * B + t % B;
+        q.len += n;
+    }
+    if (n_pairs_out) *n_pairs_out = np;
+    return PKV_OK;
+}
+
+int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t max_blocks,
+                           int32_t pad_value, int32_t *tables_out, int32_t *ctx_out) {
+    if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !tables_out || !ctx_out)))
+        return fail(PKV_EINVAL, "pkv_build_block_tables: bad arguments");
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = pool->seqs.find(seq_ids[i]);
+        if (it == pool->seqs.end())
+            return fail(PKV_ENOSEQ, "pkv_build_block_tables: unknown sequence %lld", (long long)seq_ids[i]);
+        if (static_cast<int64_t>(it->second.blocks.size()) > max_blocks)
+            return fail(PKV_EINVAL, "pkv_build_block_tables: sequence %lld has %zu blocks > max_blocks %d",
+                        (long long)seq_ids[i], it->second.blocks.size(), max_blocks);
+        if (it->second.len > INT32_MAX)
+            return fail(PKV_EINVAL, "pkv_build_block_tables: sequence %lld too long", (long long)seq_ids[i]);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const auto &q = pool->seqs.find(seq_ids[i])->second;
+        int32_t *row = tables_out + static_cast<int64_t>(i) * max_blocks;
+        size_t j = 0;
+        for (; j < q.blocks.size(); ++j) row[j] = q.blocks[j];
+        for (; j < static_cast<size_t>(max_blocks); ++j) row[j] = pad_value;
+        ctx_out[i] = static_cast<int32_t>(q.len);
+    }
+    return PKV_OK;
+}
+
+}  // extern "C"

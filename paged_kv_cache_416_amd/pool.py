@@ -1,0 +1,107 @@
+"""Python handle on the native host block-pool allocator (pkv_pool_* / pkv_seq_* in include/pkv.h)."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import PKV_ENOMEM, PkvError, check, load
+
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def _i32p(a):
+    return a.ctypes.data_as(_pi32)
+
+
+def _i64p(a):
+    return a.ctypes.data_as(_pi64)
+
+
+class OutOfBlocks(PkvError):
+    pass
+
+
+class Pool:
+    """A pool of fixed-size physical blocks with per-sequence block tables (host state)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if fo.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+        check(self._lib.pkv_pool_create(num_blocks, block_size, _i32p(fo) if fo is not None else None,
+                                        ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_pool_destroy(h)
+            self._h = None
+
+    # queries
+    def num_free(self) -> int:
+        return int(self._lib.pkv_pool_num_free(self._h))
+
+    def ref_count(self, block: int) -> int:
+        return int(self._lib.pkv_block_ref_count(self._h, block))
+
+    def length(self, sid: int) -> int:
+        n = int(self._lib.pkv_seq_len(self._h, sid))
+        if n < 0:
+            check(n)
+        return n
+
+    def blocks(self, sid: int):
+        nb = int(self._lib.pkv_seq_num_blocks(self._h, sid))
+        if nb < 0:
+            check(nb)
+        out = np.zeros(max(nb, 1), np.int32)
+        n = int(self._lib.pkv_seq_blocks(self._h, sid, _i32p(out), nb))
+        if n < 0:
+            check(n)
+        return out[:n].tolist()
+
+    # lifecycle
+    def add(self, sid: int):
+        check(self._lib.pkv_seq_add(self._h, sid))
+
+    def free(self, sid: int):
+        check(self._lib.pkv_seq_free(self._h, sid))
+
+    def fork(self, parent: int, child: int):
+        check(self._lib.pkv_seq_fork(self._h, parent, child))
+
+    def append(self, requests):
+        """requests: [(sid, n_tokens), ...] -> (slots int64 [sum n], pairs int32 [P, 2]); all or nothing."""
+        ids = np.ascontiguousarray([r[0] for r in requests], dtype=np.int64)
+        ns = np.ascontiguousarray([r[1] for r in requests], dtype=np.int32)
+        total = int(ns.sum()) if len(ns) else 0
+        slots = np.zeros(max(total, 1), np.int64)
+        max_pairs = len(requests)
+        pairs = np.zeros(2 * max(max_pairs, 1), np.int32)
+        npairs = ctypes.c_int32(0)
+        rc = self._lib.pkv_seq_append(self._h, _i64p(ids), _i32p(ns), len(requests), _i64p(slots), _i32p(pairs),
+                                      max_pairs, ctypes.byref(npairs))
+        if rc == PKV_ENOMEM:
+            raise OutOfBlocks(rc, self._lib.pkv_last_error().decode())
+        check(rc)
+        return slots[:total], pairs[:2 * npairs.value].reshape(-1, 2)
+
+    def tables(self, sids, max_blocks=None, pad=-1):
+        """Dense block tables int32 [n, max_blocks] (padded) and lengths int32 [n], host arrays."""
+        ids = np.ascontiguousarray(sids, dtype=np.int64)
+        if max_blocks is None:
+            max_blocks = max([len(self.blocks(int(s))) for s in ids] + [1])
+        tb = np.zeros((len(ids), max_blocks), np.int32)
+        ctx = np.zeros(len(ids), np.int32)
+        check(self._lib.pkv_build_block_tables(self._h, _i64p(ids), len(ids), max_blocks, pad, _i32p(tb),
+                                               _i32p(ctx)))
+        return tb, ctx

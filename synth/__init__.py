@@ -164,13 +164,13 @@ def _pool_size(blocks_needed, factor=1.1):
     return int(math.ceil(factor * blocks_needed))
 
 
-def _decode_workload(name, seed, lengths, hq, hkv, d, bs, dtype, vscale, qscale,
+def decode_workload(name, seed, lengths, hq, hkv, d, bs, dtype, vscale, qscale,
                      partition_size=0, lmax=0, scale=None, notes=None):
     """Independent sequences: prefill ctx-1 tokens each, then a one-token decode append."""
     lengths = np.asarray(lengths, dtype=np.int64)
     S = len(lengths)
     need = int(sum(-(-int(c) // bs) for c in lengths))
-    nb = _pool_size(need)
+    nb = max(1, _pool_size(need))
     free_order = _rng(seed, _FREE).permutation(nb).astype(np.int32)
     q = normal(_rng(seed, _Q), (S, hq, d), qscale, dtype)
     kv = _draw_kv(seed, _KV, [(s,) for s in range(S)], [int(c) for c in lengths], hkv, d, vscale, dtype)
@@ -178,7 +178,9 @@ def _decode_workload(name, seed, lengths, hq, hkv, d, bs, dtype, vscale, qscale,
     pre = [(s, kv[s][0][:-1], kv[s][1][:-1]) for s in range(S) if lengths[s] > 1]
     if pre:
         ops.append(("append", pre))
-    ops.append(("append", [(s, kv[s][0][-1:], kv[s][1][-1:]) for s in range(S) if lengths[s] > 0]))
+    last = [(s, kv[s][0][-1:], kv[s][1][-1:]) for s in range(S) if lengths[s] > 0]
+    if last:
+        ops.append(("append", last))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return Workload(name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
@@ -214,14 +216,14 @@ def llama13b(seed=2, num_seqs=30, ctx_range=(128, 2048), dtype="f16", block_size
              partition_size=0):
     """13B-shaped decode: 40 heads x 128 (hidden 5120), block 16, context U[128, 2048], values N(0,1)*0.5."""
     lengths = _rng(seed, _LENGTHS).integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs)
-    return _decode_workload("13b-decode", seed, lengths, 40, 40, 128, block_size, dtype, 0.5, 0.5,
+    return decode_workload("13b-decode", seed, lengths, 40, 40, 128, block_size, dtype, 0.5, 0.5,
                             partition_size=partition_size, lmax=ctx_range[1])
 
 
 def block_sweep(block_size=16, seed=4, num_seqs=64, ctx_range=(512, 4096), dtype="f16"):
     """Block-size sweep shape: 64 sequences, 40 x 128 fp16, context U[512, 4096]."""
     lengths = _rng(seed, _LENGTHS).integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs)
-    return _decode_workload(f"sweep-b{block_size}", seed, lengths, 40, 40, 128, block_size, dtype,
+    return decode_workload(f"sweep-b{block_size}", seed, lengths, 40, 40, 128, block_size, dtype,
                             0.5, 0.5, lmax=ctx_range[1])
 
 

@@ -1,0 +1,70 @@
+"""Helpers shared by the GPU parity tests: replay a workload on both sides and compare."""
+import sys
+from functools import lru_cache
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from paged_kv_cache_416_amd import kernels
+from paged_kv_cache_416_amd.cache import PagedKVCache, run_ops, to_device
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+# |gpu - ref64| <= ATOL + RTOL * |ref64|: 2e-3 for 16-bit storage, 1e-5 for fp32
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what=""):
+    g = to_f64(got)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    tol = TOL[dtype]
+    err = np.abs(g - ref)
+    bound = tol + tol * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), ref.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {ref.size} outside tolerance; worst at {i}: "
+                             f"gpu={g[i]!r} ref={ref[i]!r} err={err[i]:.3e}")
+    return float(err.max(initial=0.0))
+
+
+def cache_bytes(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+def host_bytes(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+def gpu_replay(w, on_check=None):
+    dt = TORCH_DTYPE[w.dtype]
+    c = PagedKVCache(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt, free_order=w.free_order)
+    run_ops(c, w.ops, dt, on_check=(lambda: on_check(c)) if on_check else None)
+    torch.cuda.synchronize()
+    return c
+
+
+def gpu_attention(c, w, partition_size=None, flags=0, q=None):
+    dt = TORCH_DTYPE[w.dtype]
+    qd = to_device(w.q, dt, c.device) if q is None else q
+    P = w.partition_size if partition_size is None else partition_size
+    out = c.attention(qd, w.batch, w.scale, partition_size=P, flags=flags)
+    torch.cuda.synchronize()
+    return out
+
+
+@lru_cache(maxsize=4)
+def oracle_state(key, builder, *args):
+    """Oracle replay, cached by key (workloads are deterministic)."""
+    w = builder(*args)
+    return w, oracle.replay(w)
