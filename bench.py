@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -156,6 +158,15 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": "attn_decode_kernel" + ("+attn_reduce_kernel" if P else "")},
     }
+
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
+        del src, dst
 
     if not args.no_contiguous:
         result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_avg_us)

@@ -39,7 +39,18 @@ def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what=""):
 
 
 def cache_bytes(t: torch.Tensor) -> np.ndarray:
-    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+
+
+def same_bytes(a: np.ndarray, b: np.ndarray, what="") -> bool:
+    """Byte equality of two flat uint8 arrays; on mismatch raise with the first differing offset."""
+    if a.shape != b.shape:
+        raise AssertionError(f"{what}: {a.shape} bytes vs {b.shape}")
+    diff = np.flatnonzero(a != b)
+    if diff.size:
+        i = int(diff[0])
+        raise AssertionError(f"{what}: {diff.size} bytes differ, first at offset {i}: {a[i]} vs {b[i]}")
+    return True
 
 
 def host_bytes(a: np.ndarray) -> np.ndarray:

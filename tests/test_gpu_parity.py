@@ -12,7 +12,8 @@ import synth
 from paged_kv_cache_416_amd import kernels
 from paged_kv_cache_416_amd.cache import PagedKVCache, poison_, to_device
 
-from harness import (TORCH_DTYPE, assert_close, cache_bytes, gpu_attention, gpu_replay, host_bytes, say, to_f64)
+from harness import (TORCH_DTYPE, assert_close, cache_bytes, gpu_attention, gpu_replay, host_bytes, same_bytes, say,
+                     to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,8 +73,8 @@ def _modes(w):
 def test_cache_writes_byte_identical(name):
     w, st = _case(name)
     c = gpu_replay(w)
-    assert np.array_equal(cache_bytes(c.k), host_bytes(st.k_cache)), "K cache differs"
-    assert np.array_equal(cache_bytes(c.v), host_bytes(st.v_cache)), "V cache differs"
+    same_bytes(cache_bytes(c.k), host_bytes(st.k_cache), f"{name} K cache")
+    same_bytes(cache_bytes(c.v), host_bytes(st.v_cache), f"{name} V cache")
     assert c.pool.num_free() == st.pool.num_free()
 
 
@@ -232,8 +233,8 @@ def test_reshape_and_cache_strided_views_and_padding_slots():
         vc = poison_(torch.empty_like(kc))
         kernels.reshape_and_cache(fused[:, 1], fused[:, 2], kc, vc, torch.from_numpy(slots).cuda())
         torch.cuda.synchronize()
-        assert np.array_equal(cache_bytes(kc), host_bytes(kc_o))
-        assert np.array_equal(cache_bytes(vc), host_bytes(vc_o))
+        same_bytes(cache_bytes(kc), host_bytes(kc_o), f"{dtype} K")
+        same_bytes(cache_bytes(vc), host_bytes(vc_o), f"{dtype} V")
 
 
 def test_copy_blocks_multilayer():
@@ -276,15 +277,15 @@ def test_cow_sampling_step_by_step(full):
             touched = sorted({s // w.block_size for s in slots_o} | {d for _, d in pairs_o})
             idx = torch.tensor(touched, device="cuda")
             torch.cuda.synchronize()
-            assert np.array_equal(cache_bytes(c.k.index_select(0, idx)), host_bytes(st.k_cache[touched]))
-            assert np.array_equal(cache_bytes(c.v.index_select(0, idx)), host_bytes(st.v_cache[touched]))
+            same_bytes(cache_bytes(c.k.index_select(0, idx)), host_bytes(st.k_cache[touched]), f"step {i} K")
+            same_bytes(cache_bytes(c.v.index_select(0, idx)), host_bytes(st.v_cache[touched]), f"step {i} V")
         elif op[0] == "check":
             out = gpu_attention(c, w, partition_size=0)
             assert_close(out, st.checks[-1], w.dtype, f"cow check {len(st.checks)}")
 
     st = oracle.replay(w, after_op=after)
-    assert np.array_equal(cache_bytes(c.k), host_bytes(st.k_cache))
-    assert np.array_equal(cache_bytes(c.v), host_bytes(st.v_cache))
+    same_bytes(cache_bytes(c.k), host_bytes(st.k_cache), "final K")
+    same_bytes(cache_bytes(c.v), host_bytes(st.v_cache), "final V")
     priv = np.array(w.notes["private"])
     steps = w.notes["steps"]
     if steps:
