@@ -15,6 +15,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit multiply-add fusion: every FMA is written out, so a kernel's rounding
+    # does not depend on how the optimiser happened to shape its basic blocks
+    "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["errors.cpp", "pool.cpp", "cache_ops.hip", "attention.hip"]

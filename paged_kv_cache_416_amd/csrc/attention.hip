@@ -5,24 +5,33 @@
 // the block table (slide 10). The result is ordinary single-query scaled
 // dot-product attention over the sequence's gathered context.
 //
-// Kernel design (gfx950, wave64):
-//  * one workgroup = 4 waves per (sequence, query head[, partition]);
-//  * the workgroup stages the block-table entries it needs in LDS, then each
-//    wave walks its share of blocks; the (block, kv head) tile is B rows of
-//    head_dim elements, contiguous in memory, and the wave reads it with
-//    16-byte loads, consecutive lanes on consecutive 16 bytes (1 KiB per
-//    instruction), K and V tiles of several blocks in flight at once;
-//  * a row's dot product is split over LPR lanes and finished with a
-//    cross-lane butterfly; softmax is online per wave (running max m, sum l,
-//    rescaled accumulator), in base 2 with log2(e) folded into the scale;
-//  * waves merge through LDS in a fixed order; no atomics, so results are
-//    bit-reproducible and do not depend on where blocks live;
+// Kernel design (gfx950, wave64), one workgroup of W waves per
+// (sequence, query head[, partition]):
+//  * the work unit is a tile: TR consecutive rows (tokens) of one
+//    (block, kv head), TR * head_dim contiguous elements; the tiles of the
+//    workgroup's token range are dealt round-robin to its waves;
+//  * a lane reads 16 bytes per load, consecutive lanes on consecutive 16 bytes,
+//    so one load instruction covers RPI whole rows (1 KiB for 16-bit d=128);
+//    K and V loads are non-temporal (each byte is read once);
+//  * each wave keeps 64 of its block-table entries in one register (lane i
+//    holds its i-th next entry) and moves an entry to a scalar register with
+//    readlane, so a tile's base address is scalar and no LDS or barrier sits
+//    in the loop;
+//  * loads are double-buffered in registers: the next stage's K/V loads are in
+//    flight while the current stage is consumed;
+//  * a row's dot product is split over LPR lanes (dot2 instructions for 16-bit
+//    types) and summed with DPP row operations; softmax is online per lane
+//    (running max m, sum l, rescaled accumulator) in base 2 with log2(e)
+//    folded into the scale; lanes, then waves, are merged in a fixed order at
+//    the end: no atomics, so results are bit-reproducible and do not depend on
+//    where blocks live;
 //  * rows past the context end are never loaded and are excluded by select,
 //    never multiplied by a zero weight (0 * NaN = NaN);
-//  * split mode: each partition writes (m, l, unnormalised accumulator) to
-//    an fp32 workspace and a second kernel merges them:
+//  * split mode: each partition writes (m, l, unnormalised accumulator) to an
+//    fp32 workspace and a second kernel merges them:
 //    M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
-// The contiguous-cache variant is the same template; only a tile's address differs.
+// The contiguous-cache variant is the same template; only a tile's address
+// differs.
 #include <algorithm>
 #include <cmath>
 
@@ -32,20 +41,29 @@ namespace pkv {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTableChunk = 256;  // block-table entries staged in LDS at a time
+
+__device__ inline float as_f(unsigned u) { return __uint_as_float(u); }
 
 struct F32 {
     static constexpr int VEC = 4;
     static constexpr int ELT = 4;
-    static __device__ inline void unpack(const u32x4 &r, float *f) {
-        f[0] = __uint_as_float(r.x);
-        f[1] = __uint_as_float(r.y);
-        f[2] = __uint_as_float(r.z);
-        f[3] = __uint_as_float(r.w);
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        a = fmaf(as_f(q.x), as_f(k.x), a);
+        a = fmaf(as_f(q.y), as_f(k.y), a);
+        a = fmaf(as_f(q.z), as_f(k.z), a);
+        return fmaf(as_f(q.w), as_f(k.w), a);
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        acc[0] = fmaf(p, as_f(v.x), acc[0]);
+        acc[1] = fmaf(p, as_f(v.y), acc[1]);
+        acc[2] = fmaf(p, as_f(v.z), acc[2]);
+        acc[3] = fmaf(p, as_f(v.w), acc[3]);
     }
     static __device__ inline void store(void *out, int64_t i, float x) { static_cast<float *>(out)[i] = x; }
 };
@@ -53,10 +71,20 @@ struct F32 {
 struct F16 {
     static constexpr int VEC = 8;
     static constexpr int ELT = 2;
-    static __device__ inline void unpack(const u32x4 &r, float *f) {
-        const f16x8 h = __builtin_bit_cast(f16x8, r);
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        // products of binary16 values are exact in fp32; dot2 accumulates in fp32.
+        // (Words are copied out of the vectors first: a bit_cast of a vector element
+        // lvalue reads element 0 with this compiler.)
+        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+        for (int i = 0; i < 4; ++i)
+            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[i]), __builtin_bit_cast(f16x2, kw[i]), a, false);
+        return a;
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, static_cast<float>(h[i]), acc[i]);
     }
     static __device__ inline void store(void *out, int64_t i, float x) {
         static_cast<_Float16 *>(out)[i] = static_cast<_Float16>(x);  // round to nearest even
@@ -66,12 +94,20 @@ struct F16 {
 struct BF16 {
     static constexpr int VEC = 8;
     static constexpr int ELT = 2;
-    static __device__ inline void unpack(const u32x4 &r, float *f) {
-        const unsigned w[4] = {r.x, r.y, r.z, r.w};
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[i]), __builtin_bit_cast(bf16x2, kw[i]),
+                                                a, false);
+        return a;
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            acc[2 * i] = fmaf(p, as_f(w[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(p, as_f(w[i] & 0xffff0000u), acc[2 * i + 1]);
         }
     }
     static __device__ inline void store(void *out, int64_t i, float x) {
@@ -104,21 +140,62 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
-// Main kernel: grid = (parts, num_q_heads, num_seqs), block = 256.
-// E: element type; D: head_dim; B: tokens per block (tile rows); PAGED: table lookup or contiguous slab.
-template <class E, int D, int B, bool PAGED>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(const AttnParams p) {
-    constexpr int VEC = E::VEC;         // elements per 16-byte load
-    constexpr int LPR = D / VEC;        // lanes per tile row
-    constexpr int RPI = 64 / LPR;       // tile rows per wave load instruction
-    static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "head_dim does not map onto a wave");
-    static_assert(B % RPI == 0, "block_size must be a multiple of rows per load");
-    constexpr int NL = B / RPI;         // loads per lane per tile
-    constexpr int U = NL >= 8 ? 1 : 8 / NL;  // tiles per wave iteration (K and V: 2*U*NL loads in flight)
+// DPP lane moves within a row of 16 lanes.
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
 
-    __shared__ int32_t s_tbl[PAGED ? kTableChunk : 1];
-    __shared__ float s_m[kWaves], s_l[kWaves];
-    __shared__ float s_acc[kWaves][D];
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N consecutive lanes (N = 8, 16, 32 or 64); every lane of
+// the group gets the same value (each step adds a lane's value to its partner's, and
+// floating-point addition is commutative).
+template <int N>
+__device__ inline float group_sum(float x) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ inline u32x4 nt_load(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Compile-time shape of the tile walk for element type E, head_dim D, block_size B.
+template <class E, int D, int B>
+struct Shape {
+    static constexpr int VEC = E::VEC;                  // elements per 16-byte load
+    static constexpr int LPR = D / VEC;                 // lanes per row
+    static constexpr int RPI = 64 / LPR;                // rows per load instruction
+    static constexpr int TR = B < RPI * 8 ? B : RPI * 8;  // tile rows: at most 8 loads per lane per tile
+    static constexpr int SPB = B / TR;                  // tiles per block
+    static constexpr int NL = TR / RPI;                 // loads per lane per tile (K or V)
+    static constexpr int U = NL >= 8 ? 1 : 8 / NL;      // tiles per stage
+    static constexpr int TILE_ELEMS = TR * D;
+    static_assert(LPR >= 8 && LPR <= 64 && 64 % LPR == 0, "head_dim does not map onto a wave");
+    static_assert(TR % RPI == 0 && B % TR == 0, "block_size must be a multiple of rows per load");
+    static_assert(64 % U == 0, "a stage must not straddle a table chunk");
+};
+
+// Main kernel: grid = (parts, num_q_heads, num_seqs), block = 64 * W.
+template <class E, int D, int B, bool PAGED, int W>
+__global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
+    using SH = Shape<E, D, B>;
+    constexpr int VEC = SH::VEC, LPR = SH::LPR, RPI = SH::RPI, TR = SH::TR, SPB = SH::SPB, NL = SH::NL,
+                  U = SH::U;
+    constexpr int LSTRIDE = RPI * D * E::ELT;  // bytes between a lane's loads within a tile
+
+    __shared__ float s_m[W], s_l[W];
+    __shared__ float s_acc[W][D];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -132,133 +209,192 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(const AttnParams 
     const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
     if (t0 >= t1) {  // uniform over the workgroup
         if (p.partition_size == 0)
-            for (int i = threadIdx.x; i < D; i += kThreads) E::store(p.out, row_q * D + i, 0.f);
+            for (int i = threadIdx.x; i < D; i += W * 64) E::store(p.out, row_q * D + i, 0.f);
         return;
     }
 
     const int r0 = lane / LPR, c = lane % LPR;
-    float qf[VEC];
-    {
-        const char *qp = static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT;
-        E::unpack(*reinterpret_cast<const u32x4 *>(qp), qf);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qf[e] *= p.scale_log2;
-    }
+    const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
+    const int lane_off = (r0 * D + c * VEC) * E::ELT;
+    const char *kc = static_cast<const char *>(p.k);
+    const char *vc = static_cast<const char *>(p.v);
 
-    const char *kb = static_cast<const char *>(p.k);
-    const char *vb = static_cast<const char *>(p.v);
-    const int jb = t0 / B, je = (t1 + B - 1) / B;
-    float m_w = -INFINITY, l_w = 0.f;
+    // Tiles of this workgroup: jt0 .. jt0+n-1 (tile jt covers tokens jt*TR .. jt*TR+TR-1);
+    // this wave takes tiles jt0 + wave + k*W, k = 0 .. nk-1, in stages of U tiles.
+    const int jt0 = t0 / TR;
+    const int n = (t1 + TR - 1) / TR - jt0;
+    const int nk = n > wave ? (n - wave + W - 1) / W : 0;
+    const int nst = (nk + U - 1) / U;
+
+    // Block-table chunk: lane i holds the physical block of this wave's tile kb + i.
+    const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
+    int kb = 0, tb = 0;
+    auto fetch_table = [&](int base) -> int {
+        const int k = base + lane;
+        return k < nk ? trow[(jt0 + wave + k * W) / SPB] : 0;
+    };
+
+    // Byte offset of this wave's tile k in the cache; ok = false for a table entry outside the pool.
+    auto tile_offset = [&](int k, bool &ok) -> int64_t {
+        const int jt = jt0 + wave + k * W;
+        if constexpr (PAGED) {
+            const int pb = __builtin_amdgcn_readlane(tb, k - kb);
+            ok = pb >= 0 && pb < p.num_blocks;
+            const int64_t blk = ok ? pb : 0;
+            return ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * D * E::ELT;
+        } else {
+            ok = true;
+            return ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * D *
+                   E::ELT;
+        }
+    };
+
+    struct Stage {
+        u32x4 k[U][NL], v[U][NL];
+        int tok0[U];
+        bool ok[U];
+    };
+
+    auto next_chunk = [&](int st) {
+        if constexpr (PAGED) {
+            if (st * U - kb >= 64) {
+                kb += 64;
+                tb = fetch_table(kb);
+                // Wait here, on this rare path, so that the register is known complete
+                // where the paths merge and the common path gets no wait for it.
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+        }
+    };
+
+    // Issue a stage whose tiles all exist and whose rows are all inside [t0, t1).
+    auto issue_full = [&](Stage &S, int st) {
+        next_chunk(st);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = st * U + u;
+            const int64_t off = tile_offset(k, S.ok[u]) + lane_off;
+            S.tok0[u] = (jt0 + wave + k * W) * TR;
+#pragma unroll
+            for (int l = 0; l < NL; ++l) S.k[u][l] = nt_load(kc + off + l * LSTRIDE);
+#pragma unroll
+            for (int l = 0; l < NL; ++l) S.v[u][l] = nt_load(vc + off + l * LSTRIDE);
+        }
+    };
+
+    // Issue any stage: tiles past the wave's last and rows past t1 are not loaded (zeros).
+    auto issue_tail = [&](Stage &S, int st) {
+        next_chunk(st);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = st * U + u;
+            S.tok0[u] = (jt0 + wave + k * W) * TR;
+            int64_t off = 0;
+            bool ok = false;
+            if (k < nk) off = tile_offset(k, ok) + lane_off;
+            S.ok[u] = ok;
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                const bool in = ok && S.tok0[u] + l * RPI + r0 < t1;
+                S.k[u][l] = in ? nt_load(kc + off + l * LSTRIDE) : u32x4{0u, 0u, 0u, 0u};
+                S.v[u][l] = in ? nt_load(vc + off + l * LSTRIDE) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    float m = -INFINITY, lsum = 0.f;
     float acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-    for (int cb = jb; cb < je; cb += (PAGED ? kTableChunk : (1 << 30))) {
-        const int n = PAGED ? min(kTableChunk, je - cb) : je - cb;
-        if constexpr (PAGED) {
-            __syncthreads();  // the previous chunk's entries are no longer read
-            const int32_t *trow = p.tables + static_cast<int64_t>(s) * p.max_blocks + cb;
-            for (int i = threadIdx.x; i < n; i += kThreads) s_tbl[i] = trow[i];
-            __syncthreads();
+    auto consume = [&](const Stage &S, bool tail) {
+        float sc[U][NL];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                const float d = group_sum<LPR>(E::dot(qv, S.k[u][l], 0.f)) * p.scale_log2;
+                const bool valid = S.ok[u] && (!tail || S.tok0[u] + l * RPI + r0 < t1);
+                sc[u][l] = valid ? d : -INFINITY;
+                mloc = fmaxf(mloc, sc[u][l]);
+            }
         }
-        for (int i0 = wave * U; i0 < n; i0 += kWaves * U) {
-            u32x4 kr[U][NL], vr[U][NL];
-            bool okb[U];
+        const float m_new = fmaxf(m, mloc);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // a lane with no valid row yet
+        const float alpha = fast_exp2(m - m_ref);
+        lsum *= alpha;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j = i0 + u;
-                const int tok0 = (cb + j) * B;
-                bool ok = j < n;
-                int64_t tile;
-                if constexpr (PAGED) {
-                    const int pb = ok ? s_tbl[j] : 0;
-                    ok = ok && pb >= 0 && pb < p.num_blocks;
-                    tile = (static_cast<int64_t>(pb) * p.num_kv_heads + kvh) * (B * D);
-                } else {
-                    tile = ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + tok0) * D;
-                }
-                okb[u] = ok;
+        for (int e = 0; e < VEC; ++e) acc[e] *= alpha;
 #pragma unroll
-                for (int l = 0; l < NL; ++l) {
-                    const int row = l * RPI + r0;
-                    const int64_t off = (tile + static_cast<int64_t>(row) * D + c * VEC) * E::ELT;
-                    if (ok && tok0 + row < t1) {
-                        kr[u][l] = *reinterpret_cast<const u32x4 *>(kb + off);
-                        vr[u][l] = *reinterpret_cast<const u32x4 *>(vb + off);
-                    } else {
-                        kr[u][l] = u32x4{0u, 0u, 0u, 0u};
-                        vr[u][l] = u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
+        for (int u = 0; u < U; ++u) {
+            if (!S.ok[u]) continue;  // uniform: a rejected table entry's tile is never read
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                const float pr = fast_exp2(sc[u][l] - m_ref);
+                lsum += pr;
+                E::axpy(pr, S.v[u][l], acc);
             }
-            // logits (base 2) of this iteration's rows
-            float sc[U][NL];
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tok0 = (cb + i0 + u) * B;
-#pragma unroll
-                for (int l = 0; l < NL; ++l) {
-                    float kf[VEC];
-                    E::unpack(kr[u][l], kf);
-                    float d = 0.f;
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) d = fmaf(qf[e], kf[e], d);
-#pragma unroll
-                    for (int o = LPR / 2; o > 0; o >>= 1) d += __shfl_xor(d, o);
-                    const bool ok = okb[u] && tok0 + l * RPI + r0 < t1;
-                    sc[u][l] = ok ? d : -INFINITY;
-                    mloc = fmaxf(mloc, sc[u][l]);
-                }
-            }
-#pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o));
-            const float m_new = fmaxf(m_w, mloc);
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;  // only when every tile was rejected
-            const float alpha = fast_exp2(m_w - m_ref);
-            l_w *= alpha;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[e] *= alpha;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-#pragma unroll
-                for (int l = 0; l < NL; ++l) {
-                    const float pr = fast_exp2(sc[u][l] - m_ref);
-                    l_w += pr;
-                    float vf[VEC];
-                    E::unpack(vr[u][l], vf);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pr, vf[e], acc[e]);
-                }
-            }
-            m_w = m_new;
+        }
+        m = m_new;
+    };
+
+    if (nst > 0) {
+        if constexpr (PAGED) tb = fetch_table(0);
+        Stage A, Bs;
+        int st = 0;
+        // Stages 0 .. nst-2 are full; the last may be partial. The steady-state loop only
+        // issues full stages, so every load it issues is unconditional.
+        if (nst >= 2)
+            issue_full(A, 0);
+        else
+            issue_tail(A, 0);
+        while (st + 4 <= nst) {
+            issue_full(Bs, st + 1);
+            consume(A, false);
+            issue_full(A, st + 2);
+            consume(Bs, false);
+            st += 2;
+        }
+        while (true) {
+            if (st + 1 < nst) issue_tail(Bs, st + 1);
+            consume(A, true);
+            if (++st >= nst) break;
+            if (st + 1 < nst) issue_tail(A, st + 1);
+            consume(Bs, true);
+            if (++st >= nst) break;
         }
     }
 
-    // sum over the wave's row groups: lanes with the same column chunk c
+    // Merge the lane groups that hold the same columns (different rows), in a fixed order.
 #pragma unroll
     for (int o = LPR; o < 64; o <<= 1) {
-        l_w += __shfl_xor(l_w, o);
+        const float mo = __shfl_xor(m, o), lo = __shfl_xor(lsum, o);
+        const float M = fmaxf(m, mo);
+        const float Mr = M == -INFINITY ? 0.f : M;
+        const float f1 = fast_exp2(m - Mr), f2 = fast_exp2(mo - Mr);
+        lsum = lsum * f1 + lo * f2;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], o);
+        for (int e = 0; e < VEC; ++e) acc[e] = acc[e] * f1 + __shfl_xor(acc[e], o) * f2;
+        m = M;
     }
     if (lane < LPR) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) s_acc[wave][c * VEC + e] = acc[e];
     }
     if (lane == 0) {
-        s_m[wave] = m_w;
-        s_l[wave] = l_w;
+        s_m[wave] = m;
+        s_l[wave] = lsum;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < D; i += kThreads) {
+    for (int i = threadIdx.x; i < D; i += W * 64) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w]);
         const float Mr = M == -INFINITY ? 0.f : M;
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float f = fast_exp2(s_m[w] - Mr);
             L = fmaf(s_l[w], f, L);
             O = fmaf(s_acc[w][i], f, O);
@@ -300,7 +436,7 @@ __global__ __launch_bounds__(D) void attn_reduce_kernel(const AttnParams p) {
 
 template <class E, int D, int B, bool PAGED>
 int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED>), dim3(grid_parts, p.num_q_heads, num_seqs),
+    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves>), dim3(grid_parts, p.num_q_heads, num_seqs),
                        dim3(kThreads), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "attention launch");
     if (rc || p.partition_size == 0) return rc;
@@ -416,6 +552,7 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
                     block_size);
     if (!block_tables || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "%s: block_tables NULL or max_blocks_per_seq / num_blocks not positive", fn);
+    if (num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: num_blocks %lld exceeds int32", fn, (long long)num_blocks);
     (void)flags;
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
     AttnParams p = make_params(out, q, k_cache, v_cache, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
