@@ -45,7 +45,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
 __device__ inline float as_f(unsigned u) { return __uint_as_float(u); }
@@ -200,39 +200,40 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int kvh = h / p.group;
-    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-    int t0 = 0, t1 = ctx;
-    if (p.partition_size > 0) {
-        t0 = part * p.partition_size;
-        t1 = min(ctx, t0 + p.partition_size);
-    }
     const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
+    const int r0 = lane / LPR, c = lane % LPR;
+    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
+
+    // Tiles of this workgroup: jt0 .. jt0+n-1 (tile jt covers tokens jt*TR .. jt*TR+TR-1);
+    // this wave takes tiles jt0 + wave + k*W, k = 0 .. nk-1, in stages of U tiles.
+    const int jt0 = t0 / TR;
+
+    // Block-table chunk: lane i holds the physical block of this wave's tile kb + i. The
+    // first chunk is requested together with the length and the query (it depends on
+    // neither); entries past the sequence's last block are read but never used.
+    const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
+    int kb = 0, tb = 0;
+    auto fetch_table = [&](int base) -> int {
+        const int j = (jt0 + wave + (base + lane) * W) / SPB;
+        return j < p.max_blocks ? trow[j] : 0;
+    };
+    if constexpr (PAGED) tb = fetch_table(0);
+    const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
+
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
     if (t0 >= t1) {  // uniform over the workgroup
         if (p.partition_size == 0)
             for (int i = threadIdx.x; i < D; i += W * 64) E::store(p.out, row_q * D + i, 0.f);
         return;
     }
 
-    const int r0 = lane / LPR, c = lane % LPR;
-    const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
     const int lane_off = (r0 * D + c * VEC) * E::ELT;
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
-
-    // Tiles of this workgroup: jt0 .. jt0+n-1 (tile jt covers tokens jt*TR .. jt*TR+TR-1);
-    // this wave takes tiles jt0 + wave + k*W, k = 0 .. nk-1, in stages of U tiles.
-    const int jt0 = t0 / TR;
     const int n = (t1 + TR - 1) / TR - jt0;
     const int nk = n > wave ? (n - wave + W - 1) / W : 0;
     const int nst = (nk + U - 1) / U;
-
-    // Block-table chunk: lane i holds the physical block of this wave's tile kb + i.
-    const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
-    int kb = 0, tb = 0;
-    auto fetch_table = [&](int base) -> int {
-        const int k = base + lane;
-        return k < nk ? trow[(jt0 + wave + k * W) / SPB] : 0;
-    };
 
     // Byte offset of this wave's tile k in the cache; ok = false for a table entry outside the pool.
     auto tile_offset = [&](int k, bool &ok) -> int64_t {
@@ -340,7 +341,6 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     };
 
     if (nst > 0) {
-        if constexpr (PAGED) tb = fetch_table(0);
         Stage A, Bs;
         int st = 0;
         // Stages 0 .. nst-2 are full; the last may be partial. The steady-state loop only
