@@ -4,15 +4,23 @@
 One step = the decode step's device work on inputs resident in HBM:
   reshape_and_cache (write each sequence's new token into its slot)
   + paged_attention_decode (one query token per sequence over its paged context)
-on the 13B-shaped workload (40 heads x 128, fp16, block 16, 30 sequences, context U[128, 2048]).
-Slot assignment for the step is done once by the host allocator before timing.
+on the 13B-shaped workload by default (40 heads x 128, fp16, block 16, 30 sequences,
+context U[128, 2048]). Slot assignment for the step is done once by the host allocator
+before timing.
 
-Prints ONE JSON line. KV GB/s counts algorithmic bytes (each context token's K and V rows once,
-q in, out, table entries, lengths; plus the new tokens' K/V read and written).
+Prints ONE JSON line. GB/s counts algorithmic bytes: each context token's K and V rows once
+(for shared blocks, each physical block once: the unique bytes), q in, out, table entries and
+lengths; plus the new tokens' K/V read and written by reshape_and_cache.
+
+Helper modes (no GPU needed) turn rocprofv3 CSV output into the short text summaries kept
+under profiles/:
+  bench.py --summarize-trace KERNEL_STATS_CSV OUT_TXT "COMMAND"
+  bench.py --summarize-counters FETCH_CSV WRITE_CSV OUT_TXT "FETCH_COMMAND" "WRITE_COMMAND"
 """
 import argparse
+import csv
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -23,14 +31,41 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and decode tokens/s, 13B shape"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/common.h"]
+PROFILES = os.path.join(ROOT, "profiles")
+# attention kernel name prefix -> counters summary for the default workload
+COUNTERS_FILE = {"13b-decode": "attn_decode_f16_13b_counters.txt"}
 
 
-def attention_bytes(ctx, hq, hkv, d, elt, bs):
-    """Algorithmic bytes of one decode-attention call."""
-    kv = sum(int(c) for c in ctx) * 2 * hkv * d * elt
-    qo = 2 * len(ctx) * hq * d * elt
-    tables = sum(-(-int(c) // bs) for c in ctx) * 4
-    return kv + qo + tables + 4 * len(ctx)
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def attention_bytes(ctx, hq, hkv, d, elt, bs, unique_blocks=None):
+    """Algorithmic bytes of one decode-attention call: (logical, unique).
+
+    logical: every sequence's K and V rows; unique: each physical block's rows once, at the
+    number of rows the longest sequence mapping it uses (equal to logical without sharing)."""
+    kv_row = 2 * hkv * d * elt
+    logical_kv = sum(int(c) for c in ctx) * kv_row
+    unique_kv = logical_kv if unique_blocks is None else sum(unique_blocks.values()) * kv_row
+    other = 2 * len(ctx) * hq * d * elt + sum(-(-int(c) // bs) for c in ctx) * 4 + 4 * len(ctx)
+    return logical_kv + other, unique_kv + other
+
+
+def unique_rows(tables, ctx, bs):
+    """Physical block -> rows used, over all sequences (shared blocks counted once)."""
+    rows = {}
+    for t, c in zip(tables, ctx):
+        c = int(c)
+        for j in range(-(-c // bs)):
+            b = int(t[j])
+            rows[b] = max(rows.get(b, 0), min(bs, c - j * bs))
+    return rows
 
 
 def parse():
@@ -46,7 +81,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
+                    help="after timing, run a plain elementwise kernel over this many MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "CMD"))
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "CMD1", "CMD2"))
     return ap.parse_args()
 
 
@@ -61,11 +98,47 @@ def make_workload(name):
     raise ValueError(name)
 
 
+def timed_launches(fn, n, stream):
+    """Average device time of one launch of fn(i): HIP events on the launch stream around n
+    back-to-back launches (the gaps between them included)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / n
+
+
+def read_counters(workload):
+    """Measured HBM bytes per attention launch from the committed counter summary, if it was
+    taken on the attention source as it is now; else None."""
+    name = COUNTERS_FILE.get(workload)
+    path = os.path.join(PROFILES, name) if name else None
+    if not path or not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != attn_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_dispatch"])
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the path shards by sequence "
-              f"or KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The path shards by sequence or by "
+              f"KV head with no exchange between GPUs, so one GPU's figure at its share of the batch is the "
+              f"per-GPU figure.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -90,7 +163,10 @@ def main():
     new_k = to_device(np.concatenate([k for _, k, _ in step]), dt, dev)
     new_v = to_device(np.concatenate([v for _, _, v in step]), dt, dev)
     slot_dev = torch.from_numpy(slots).to(dev)
-    tb, ctx_dev, max_ctx = cache.tables(w.batch)
+    tb_host, ctx_host = cache.pool.tables(w.batch)
+    tb = torch.from_numpy(tb_host).to(dev)
+    ctx_dev = torch.from_numpy(ctx_host).to(dev)
+    max_ctx = int(ctx_host.max())
     ctx = w.final_lengths()
     q = to_device(w.q, dt, dev)
     out = torch.empty_like(q)
@@ -99,40 +175,35 @@ def main():
     vs = [cache.v] + [cache.v.clone() for _ in range(args.replicas - 1)]
     torch.cuda.synchronize()
 
-    a_bytes = attention_bytes(ctx, hq, hkv, d, elt, B)
+    logical_b, unique_b = attention_bytes(ctx, hq, hkv, d, elt, B, unique_rows(tb_host, ctx_host, B))
     w_bytes = 2 * 2 * len(step) * hkv * d * elt + 8 * len(step)  # K1: read + write K and V, slots
     stream = torch.cuda.current_stream()
 
-    def one_step(i, ev=None):
+    def attend(i):
+        r = i % args.replicas
+        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, args.flags)
+
+    def one_step(i):
         r = i % args.replicas
         kernels.reshape_and_cache(new_k, new_v, ks[r], vs[r], slot_dev)
-        if ev is not None:
-            ev[0].record(stream)
-        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, args.flags)
-        if ev is not None:
-            ev[1].record(stream)
+        attend(i)
 
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
-    # timed region: whole steps, host clock
+    # timed region: exactly `steps` whole steps, synchronised on both sides, host clock
     t0 = time.perf_counter()
     for i in range(args.steps):
         one_step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # attention launches alone, HIP events on the launch stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        one_step(i, evs[i])
-    torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg_us = 1e3 * sum(attn_ms) / len(attn_ms)
-    attn_med_us = 1e3 * sorted(attn_ms)[len(attn_ms) // 2]
+    # the attention launches alone, for the roofline
+    attn_us = timed_launches(attend, args.steps, stream)
 
-    value = (a_bytes + w_bytes) / (ms_per_step * 1e-3) / 1e9
-    achieved = a_bytes / (attn_avg_us * 1e-6) / 1e9
+    value = (unique_b + w_bytes) / (ms_per_step * 1e-3) / 1e9
+    achieved = unique_b / (attn_us * 1e-6) / 1e9
+    traffic = read_counters(w.name) if P == 0 and args.flags == 0 else None
 
     result = {
         "metric": METRIC,
@@ -146,33 +217,36 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1)*0.5 keys/values, uniform context lengths)",
+        "data": "synthetic (seeded N(0,1)*0.5 keys/values, seeded context lengths and physical block order)",
         "config": {"workload": w.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": B, "sum_context": int(ctx.sum()), "max_context": int(ctx.max()),
                    "partition_size": P, "replicas": args.replicas},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
-        "attention_us": {"avg": round(attn_avg_us, 2), "median": round(attn_med_us, 2)},
-        "bytes_per_step": {"attention": a_bytes, "cache_write": w_bytes},
+        "attention_us": round(attn_us, 2),
+        "bytes_per_step": {"attention_logical": logical_b, "attention_unique": unique_b, "cache_write": w_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
                      "kernel": "attn_decode_kernel" + ("+attn_reduce_kernel" if P else "")},
     }
 
     if args.copy_probe:
+        # a plain elementwise kernel that reads and writes a known number of bytes, by which the
+        # HBM byte counters are calibrated (its kernel name contains "neg")
         src = torch.empty(args.copy_probe << 18, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         result["copy_probe_bytes"] = {"read": src.numel() * 4, "write": dst.numel() * 4}
         del src, dst
 
     if not args.no_contiguous:
-        result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_avg_us)
+        result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_us)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, P, a_bytes, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, P, unique_b, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 
@@ -205,18 +279,14 @@ def contiguous_leg(w, P, args, dev, dt, paged_us):
     cd = torch.from_numpy(ctx).to(dev)
     ws = kernels.alloc_workspace(S, w.num_q_heads, w.head_dim, lmax, P, dev)
     stream = torch.cuda.current_stream()
-    n = max(20, args.steps)
+
+    def attend(i):
+        r = i % args.replicas
+        kernels.contiguous_attention_decode(out, q, kd[r], vd[r], cd, lmax, w.scale, P, ws, args.flags)
+
     for i in range(10):
-        kernels.contiguous_attention_decode(out, q, kd[i % args.replicas], vd[i % args.replicas], cd, lmax, w.scale, P,
-                                            ws, args.flags)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for i in range(n):
-        evs[i][0].record(stream)
-        kernels.contiguous_attention_decode(out, q, kd[i % args.replicas], vd[i % args.replicas], cd, lmax, w.scale, P,
-                                            ws, args.flags)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / n
+        attend(i)
+    us = timed_launches(attend, max(20, args.steps), stream)
     return {"attention_us": round(us, 2), "paged_over_contiguous": round(paged_us / us - 1.0, 4)}
 
 
@@ -236,6 +306,67 @@ def cpu_baseline(w, P, a_bytes, seconds):
             "kind": "oracle", "sample": f"the full {w.name} batch ({w.num_seqs} sequences), {reps} calls in "
                                         f"{t:.1f} s, {per_call * 1e3:.1f} ms per call",
             "decode_tokens_per_s": round(w.num_seqs / per_call, 2)}
+
+
+# ---------------------------------------------------------------- profile summaries (no GPU)
+
+def _short(name):
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0][:110]
+
+
+def summarize_trace(stats_csv, out, cmd):
+    """rocprofv3 --kernel-trace --stats kernel table -> a short text summary."""
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel-trace summary (durations in microseconds)",
+             f"# command: {cmd}",
+             f"{'kernel':<112} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}"]
+    for r in rows:
+        lines.append(f"{_short(r['Name']):<112} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.2f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_counters(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
+    """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) -> HBM bytes per attention
+    launch, each counter scaled by what it reads for a plain elementwise kernel over a known size."""
+    def per_kernel(path):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    probe = [k for k in fetch if "neg_kernel" in k]
+    attn = [k for k in fetch if "attn_decode_kernel" in k]
+    if len(probe) != 1 or len(attn) != 1:
+        raise SystemExit(f"expected one probe and one attention kernel, got {probe} / {attn}")
+    probe_bytes = 1 << 30  # --copy-probe 1024: 1 GiB read, 1 GiB written
+    pf, pw = max(fetch[probe[0]]), max(write[probe[0]])
+    fs, wsc = probe_bytes / (pf * 1024), probe_bytes / (pw * 1024)
+    af = sum(fetch[attn[0]]) / len(fetch[attn[0]])
+    aw = sum(write[attn[0]]) / len(write[attn[0]])
+    traffic = af * 1024 * fs + aw * 1024 * wsc
+    lines = ["# HBM bytes of the attention kernel, from two rocprofv3 --pmc passes (counters in KiB per dispatch)",
+             f"# command (FETCH_SIZE): {cmd_fetch}",
+             f"# command (WRITE_SIZE): {cmd_write}",
+             "# scale = bytes the calibration kernel (torch.neg over 1 GiB: 1 GiB read, 1 GiB written) moved,",
+             "#         divided by what the counter reported for it",
+             f"kernel: {_short(attn[0])}",
+             f"kernel_source_sha256: {attn_source_hash()}",
+             f"dispatches: {len(fetch[attn[0]])}",
+             f"fetch_kib_per_dispatch: {af:.1f}",
+             f"write_kib_per_dispatch: {aw:.1f}",
+             f"probe_fetch_kib: {pf:.1f}",
+             f"probe_write_kib: {pw:.1f}",
+             f"fetch_scale: {fs:.4f}",
+             f"write_scale: {wsc:.4f}",
+             f"traffic_bytes_per_dispatch: {traffic:.0f}"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
