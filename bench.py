@@ -31,7 +31,8 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and decode tokens/s, 13B shape"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
-ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/common.h"]
+ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/attention.h",
+                "paged_kv_cache_416_amd/csrc/common.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 # attention kernel name prefix -> counters summary for the default workload
 COUNTERS_FILE = {"13b-decode": "attn_decode_f16_13b_counters.txt"}

@@ -1,0 +1,147 @@
+// Device-side pieces shared by the decode-attention kernels: element traits, launch
+// parameters, lane helpers. Internal to libpkv (not part of the C ABI).
+#pragma once
+
+#include "common.h"
+
+namespace pkv {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+
+__device__ inline float as_f(unsigned u) { return __uint_as_float(u); }
+
+struct F32 {
+    static constexpr int VEC = 4;
+    static constexpr int ELT = 4;
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        a = fmaf(as_f(q.x), as_f(k.x), a);
+        a = fmaf(as_f(q.y), as_f(k.y), a);
+        a = fmaf(as_f(q.z), as_f(k.z), a);
+        return fmaf(as_f(q.w), as_f(k.w), a);
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        acc[0] = fmaf(p, as_f(v.x), acc[0]);
+        acc[1] = fmaf(p, as_f(v.y), acc[1]);
+        acc[2] = fmaf(p, as_f(v.z), acc[2]);
+        acc[3] = fmaf(p, as_f(v.w), acc[3]);
+    }
+    static __device__ inline void store(void *out, int64_t i, float x) { static_cast<float *>(out)[i] = x; }
+};
+
+struct F16 {
+    static constexpr int VEC = 8;
+    static constexpr int ELT = 2;
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        // products of binary16 values are exact in fp32; dot2 accumulates in fp32.
+        // (Words are copied out of the vectors first: a bit_cast of a vector element
+        // lvalue reads element 0 with this compiler.)
+        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[i]), __builtin_bit_cast(f16x2, kw[i]), a, false);
+        return a;
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, static_cast<float>(h[i]), acc[i]);
+    }
+    static __device__ inline void store(void *out, int64_t i, float x) {
+        static_cast<_Float16 *>(out)[i] = static_cast<_Float16>(x);  // round to nearest even
+    }
+};
+
+struct BF16 {
+    static constexpr int VEC = 8;
+    static constexpr int ELT = 2;
+    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
+        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[i]), __builtin_bit_cast(bf16x2, kw[i]),
+                                                a, false);
+        return a;
+    }
+    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(p, as_f(w[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(p, as_f(w[i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+    }
+    static __device__ inline void store(void *out, int64_t i, float x) {
+        static_cast<__bf16 *>(out)[i] = static_cast<__bf16>(x);  // round to nearest even
+    }
+};
+
+struct AttnParams {
+    void *out;
+    const void *q;
+    const void *k;
+    const void *v;
+    const int32_t *tables;
+    const int32_t *ctx_lens;
+    float *ws;             // split workspace: acc [S*Hq*P][D], then m [S*Hq*P], then l [S*Hq*P]
+    int64_t ws_rows;       // S * Hq * num_parts
+    uint32_t num_blocks;   // paged: pool size (< 2^31)
+    int32_t max_blocks;    // paged: table row stride
+    int32_t lmax;          // contiguous: rows per (sequence, kv head)
+    int32_t ctx_cap;       // lengths are clamped to [0, ctx_cap]
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;         // num_q_heads / num_kv_heads
+    int32_t partition_size;  // 0 = single pass
+    int32_t num_parts;       // workspace parts per (sequence, head)
+    float scale_log2;        // scale * log2(e)
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+// DPP lane moves within a row of 16 lanes.
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N consecutive lanes (N = 8, 16, 32 or 64); every lane of
+// the group gets the same value (each step adds a lane's value to its partner's, and
+// floating-point addition is commutative).
+template <int N>
+__device__ inline float group_sum(float x) {
+    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    if constexpr (N >= 16) x += dpp<kRowMirror>(x);
+    if constexpr (N >= 32) x += __shfl_xor(x, 16);
+    if constexpr (N >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ inline u32x4 nt_load(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Compile-time shape of the tile walk for element type E, head_dim D, block_size B.
+
+// MFMA grouped-query kernel (attention_gqa.hip). gqa_mfma_supported tells whether a shape has
+// an MFMA build; launch_gqa_mfma enqueues it (and the reduce pass in split mode).
+bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int32_t num_seqs,
+                    int32_t grid_parts, hipStream_t stream);
+// The partition merge (attention.hip), shared by both kernels.
+int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t num_seqs, hipStream_t stream);
+
+}  // namespace pkv

@@ -35,142 +35,14 @@
 #include <algorithm>
 #include <cmath>
 
-#include "common.h"
+#include "attention.h"
 
 namespace pkv {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
-__device__ inline float as_f(unsigned u) { return __uint_as_float(u); }
-
-struct F32 {
-    static constexpr int VEC = 4;
-    static constexpr int ELT = 4;
-    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
-        a = fmaf(as_f(q.x), as_f(k.x), a);
-        a = fmaf(as_f(q.y), as_f(k.y), a);
-        a = fmaf(as_f(q.z), as_f(k.z), a);
-        return fmaf(as_f(q.w), as_f(k.w), a);
-    }
-    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
-        acc[0] = fmaf(p, as_f(v.x), acc[0]);
-        acc[1] = fmaf(p, as_f(v.y), acc[1]);
-        acc[2] = fmaf(p, as_f(v.z), acc[2]);
-        acc[3] = fmaf(p, as_f(v.w), acc[3]);
-    }
-    static __device__ inline void store(void *out, int64_t i, float x) { static_cast<float *>(out)[i] = x; }
-};
-
-struct F16 {
-    static constexpr int VEC = 8;
-    static constexpr int ELT = 2;
-    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
-        // products of binary16 values are exact in fp32; dot2 accumulates in fp32.
-        // (Words are copied out of the vectors first: a bit_cast of a vector element
-        // lvalue reads element 0 with this compiler.)
-        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw[i]), __builtin_bit_cast(f16x2, kw[i]), a, false);
-        return a;
-    }
-    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
-        const f16x8 h = __builtin_bit_cast(f16x8, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, static_cast<float>(h[i]), acc[i]);
-    }
-    static __device__ inline void store(void *out, int64_t i, float x) {
-        static_cast<_Float16 *>(out)[i] = static_cast<_Float16>(x);  // round to nearest even
-    }
-};
-
-struct BF16 {
-    static constexpr int VEC = 8;
-    static constexpr int ELT = 2;
-    static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
-        const unsigned qw[4] = {q.x, q.y, q.z, q.w}, kw[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[i]), __builtin_bit_cast(bf16x2, kw[i]),
-                                                a, false);
-        return a;
-    }
-    static __device__ inline void axpy(float p, const u32x4 &v, float *acc) {
-        const unsigned w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = fmaf(p, as_f(w[i] << 16), acc[2 * i]);
-            acc[2 * i + 1] = fmaf(p, as_f(w[i] & 0xffff0000u), acc[2 * i + 1]);
-        }
-    }
-    static __device__ inline void store(void *out, int64_t i, float x) {
-        static_cast<__bf16 *>(out)[i] = static_cast<__bf16>(x);  // round to nearest even
-    }
-};
-
-struct AttnParams {
-    void *out;
-    const void *q;
-    const void *k;
-    const void *v;
-    const int32_t *tables;
-    const int32_t *ctx_lens;
-    float *ws;             // split workspace: acc [S*Hq*P][D], then m [S*Hq*P], then l [S*Hq*P]
-    int64_t num_blocks;    // paged: pool size
-    int64_t ws_rows;       // S * Hq * num_parts
-    int32_t max_blocks;    // paged: table row stride
-    int32_t lmax;          // contiguous: rows per (sequence, kv head)
-    int32_t ctx_cap;       // lengths are clamped to [0, ctx_cap]
-    int32_t num_q_heads;
-    int32_t num_kv_heads;
-    int32_t group;         // num_q_heads / num_kv_heads
-    int32_t partition_size;  // 0 = single pass
-    int32_t num_parts;       // workspace parts per (sequence, head)
-    float scale_log2;        // scale * log2(e)
-};
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
-
-// DPP lane moves within a row of 16 lanes.
-constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7-i within each 8 lanes
-constexpr int kRowMirror = 0x140;     // lane i <- lane 15-i within each 16 lanes
-
-template <int CTRL>
-__device__ inline float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over each aligned group of N consecutive lanes (N = 8, 16, 32 or 64); every lane of
-// the group gets the same value (each step adds a lane's value to its partner's, and
-// floating-point addition is commutative).
-template <int N>
-__device__ inline float group_sum(float x) {
-    static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
-    x += dpp<kQuadSwap1>(x);
-    x += dpp<kQuadSwap2>(x);
-    x += dpp<kRowHalfMirror>(x);
-    if constexpr (N >= 16) x += dpp<kRowMirror>(x);
-    if constexpr (N >= 32) x += __shfl_xor(x, 16);
-    if constexpr (N >= 64) x += __shfl_xor(x, 32);
-    return x;
-}
-
-__device__ inline u32x4 nt_load(const char *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-// Compile-time shape of the tile walk for element type E, head_dim D, block_size B.
 template <class E, int D, int B>
 struct Shape {
     static constexpr int VEC = E::VEC;                  // elements per 16-byte load
@@ -192,12 +64,12 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     using SH = Shape<E, D, B>;
     constexpr int VEC = SH::VEC, LPR = SH::LPR, RPI = SH::RPI, TR = SH::TR, SPB = SH::SPB, NL = SH::NL,
                   U = SH::U;
-    constexpr int LSTRIDE = RPI * D * E::ELT;  // bytes between a lane's loads within a tile
 
     __shared__ float s_m[W], s_l[W];
     __shared__ float s_acc[W][D];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int kvh = h / p.group;
     const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
@@ -212,7 +84,7 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     // first chunk is requested together with the length and the query (it depends on
     // neither); entries past the sequence's last block are read but never used.
     const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
-    int kb = 0, tb = 0;
+    int tb = 0;
     auto fetch_table = [&](int base) -> int {
         const int j = (jt0 + wave + (base + lane) * W) / SPB;
         return j < p.max_blocks ? trow[j] : 0;
@@ -228,19 +100,18 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         return;
     }
 
-    const int lane_off = (r0 * D + c * VEC) * E::ELT;
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
     const int n = (t1 + TR - 1) / TR - jt0;
-    const int nk = n > wave ? (n - wave + W - 1) / W : 0;
-    const int nst = (nk + U - 1) / U;
+    const int nk = n > wave ? (n - wave + W - 1) / W : 0;  // tiles of this wave
 
-    // Byte offset of this wave's tile k in the cache; ok = false for a table entry outside the pool.
-    auto tile_offset = [&](int k, bool &ok) -> int64_t {
+    // Byte offset of this wave's tile k, whose table entry is lane k - kc0 of the current
+    // chunk; ok = false for a table entry outside the pool.
+    auto tile_offset = [&](int k, int kc0, bool &ok) -> int64_t {
         const int jt = jt0 + wave + k * W;
         if constexpr (PAGED) {
-            const int pb = __builtin_amdgcn_readlane(tb, k - kb);
-            ok = pb >= 0 && pb < p.num_blocks;
+            const int pb = __builtin_amdgcn_readlane(tb, k - kc0);
+            ok = static_cast<uint32_t>(pb) < p.num_blocks;  // 32-bit, so it stays a scalar compare
             const int64_t blk = ok ? pb : 0;
             return ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * D * E::ELT;
         } else {
@@ -253,52 +124,29 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     struct Stage {
         u32x4 k[U][NL], v[U][NL];
         int tok0[U];
-        bool ok[U];
+        bool ok[U];  // table entry inside the pool
+        bool in[U];  // tile belongs to this wave (false: a stand-in, masked out)
     };
 
-    auto next_chunk = [&](int st) {
-        if constexpr (PAGED) {
-            if (st * U - kb >= 64) {
-                kb += 64;
-                tb = fetch_table(kb);
-                // Wait here, on this rare path, so that the register is known complete
-                // where the paths merge and the common path gets no wait for it.
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-        }
-    };
-
-    // Issue a stage whose tiles all exist and whose rows are all inside [t0, t1).
-    auto issue_full = [&](Stage &S, int st) {
-        next_chunk(st);
+    // Every load is unconditional, so the compiler's wait counts stay exact. With clamp set, a
+    // tile past the wave's last is replaced by its last tile and a row at or past t1 by the
+    // row before t1: both in bounds and written; consume() masks them out.
+    auto issue = [&](Stage &S, int kc0, int st, bool clamp) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = st * U + u;
-            const int64_t off = tile_offset(k, S.ok[u]) + lane_off;
+            int k = kc0 + st * U + u;
+            S.in[u] = k < nk;
+            if (clamp) k = min(k, nk - 1);
+            const int64_t tile = tile_offset(k, kc0, S.ok[u]);
+            const char *kt = kc + tile, *vt = vc + tile;  // uniform: a scalar base for the loads
             S.tok0[u] = (jt0 + wave + k * W) * TR;
-#pragma unroll
-            for (int l = 0; l < NL; ++l) S.k[u][l] = nt_load(kc + off + l * LSTRIDE);
-#pragma unroll
-            for (int l = 0; l < NL; ++l) S.v[u][l] = nt_load(vc + off + l * LSTRIDE);
-        }
-    };
-
-    // Issue any stage: tiles past the wave's last and rows past t1 are not loaded (zeros).
-    auto issue_tail = [&](Stage &S, int st) {
-        next_chunk(st);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = st * U + u;
-            S.tok0[u] = (jt0 + wave + k * W) * TR;
-            int64_t off = 0;
-            bool ok = false;
-            if (k < nk) off = tile_offset(k, ok) + lane_off;
-            S.ok[u] = ok;
+            const int lim = t1 - 1 - S.tok0[u];  // last row inside the context
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
-                const bool in = ok && S.tok0[u] + l * RPI + r0 < t1;
-                S.k[u][l] = in ? nt_load(kc + off + l * LSTRIDE) : u32x4{0u, 0u, 0u, 0u};
-                S.v[u][l] = in ? nt_load(vc + off + l * LSTRIDE) : u32x4{0u, 0u, 0u, 0u};
+                const unsigned row = clamp ? min(l * RPI + r0, lim) : l * RPI + r0;
+                const unsigned off = row * (D * E::ELT) + c * (VEC * E::ELT);
+                S.k[u][l] = nt_load(kt + off);
+                S.v[u][l] = nt_load(vt + off);
             }
         }
     };
@@ -316,7 +164,7 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 const float d = group_sum<LPR>(E::dot(qv, S.k[u][l], 0.f)) * p.scale_log2;
-                const bool valid = S.ok[u] && (!tail || S.tok0[u] + l * RPI + r0 < t1);
+                const bool valid = S.ok[u] && (!tail || (S.in[u] && S.tok0[u] + l * RPI + r0 < t1));
                 sc[u][l] = valid ? d : -INFINITY;
                 mloc = fmaxf(mloc, sc[u][l]);
             }
@@ -329,7 +177,8 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         for (int e = 0; e < VEC; ++e) acc[e] *= alpha;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (!S.ok[u]) continue;  // uniform: a rejected table entry's tile is never read
+            // uniform: a rejected table entry's tile and a stand-in tile are never accumulated
+            if (!S.ok[u] || (tail && !S.in[u])) continue;
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 const float pr = fast_exp2(sc[u][l] - m_ref);
@@ -340,29 +189,46 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         m = m_new;
     };
 
-    if (nst > 0) {
+    // The wave's tiles in chunks of 64 (one table register each); within a chunk, stages of U
+    // tiles are double-buffered. All stages but a wave's last are full (every tile exists and
+    // every row is inside the context), so the steady-state loop needs no clamping or masks.
+    for (int kc0 = 0; kc0 < nk; kc0 += 64) {
+        if constexpr (PAGED) {
+            if (kc0 > 0) tb = fetch_table(kc0);
+        }
+        const int nst = (min(64, nk - kc0) + U - 1) / U;
+        const bool last_chunk = kc0 + 64 >= nk;
         Stage A, Bs;
         int st = 0;
-        // Stages 0 .. nst-2 are full; the last may be partial. The steady-state loop only
-        // issues full stages, so every load it issues is unconditional.
-        if (nst >= 2)
-            issue_full(A, 0);
-        else
-            issue_tail(A, 0);
+        issue(A, kc0, 0, last_chunk && nst < 2);
         while (st + 4 <= nst) {
-            issue_full(Bs, st + 1);
+            issue(Bs, kc0, st + 1, false);
             consume(A, false);
-            issue_full(A, st + 2);
+            // keep the next stage's loads behind this consume: two stages in registers, not three
+            __builtin_amdgcn_sched_barrier(0);
+            issue(A, kc0, st + 2, false);
             consume(Bs, false);
+            __builtin_amdgcn_sched_barrier(0);
             st += 2;
         }
-        while (true) {
-            if (st + 1 < nst) issue_tail(Bs, st + 1);
+        // 1 to 3 stages remain (A holds the first); straight-line code per case keeps every
+        // issue unconditional
+        switch (nst - st) {
+        case 1:
             consume(A, true);
-            if (++st >= nst) break;
-            if (st + 1 < nst) issue_tail(A, st + 1);
+            break;
+        case 2:
+            issue(Bs, kc0, st + 1, true);
+            consume(A, true);
             consume(Bs, true);
-            if (++st >= nst) break;
+            break;
+        default:
+            issue(Bs, kc0, st + 1, true);
+            consume(A, true);
+            issue(A, kc0, st + 2, true);
+            consume(Bs, true);
+            consume(A, true);
+            break;
         }
     }
 
@@ -438,39 +304,52 @@ template <class E, int D, int B, bool PAGED>
 int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves>), dim3(grid_parts, p.num_q_heads, num_seqs),
                        dim3(kThreads), 0, stream, p);
-    int rc = hip_status(hipGetLastError(), "attention launch");
-    if (rc || p.partition_size == 0) return rc;
-    hipLaunchKernelGGL((attn_reduce_kernel<E, D>), dim3(p.num_q_heads, num_seqs), dim3(D), 0, stream, p);
-    return hip_status(hipGetLastError(), "attention reduce launch");
+    return hip_status(hipGetLastError(), "attention launch");
 }
 
 template <class E, int D, bool PAGED>
 int dispatch_block(const AttnParams &p, int32_t block_size, int32_t num_seqs, int32_t grid_parts,
                    hipStream_t stream) {
-    switch (block_size) {
-    case 8: return launch<E, D, 8, PAGED>(p, num_seqs, grid_parts, stream);
-    case 16: return launch<E, D, 16, PAGED>(p, num_seqs, grid_parts, stream);
-    case 32: return launch<E, D, 32, PAGED>(p, num_seqs, grid_parts, stream);
-    default: return fail(PKV_EUNSUPPORTED, "block_size %d not built (8, 16, 32)", block_size);
+    if constexpr (!PAGED) {
+        return launch<E, D, 16, false>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+    } else {
+        switch (block_size) {
+        case 8: return launch<E, D, 8, true>(p, num_seqs, grid_parts, stream);
+        case 16: return launch<E, D, 16, true>(p, num_seqs, grid_parts, stream);
+        case 32: return launch<E, D, 32, true>(p, num_seqs, grid_parts, stream);
+        default: return fail(PKV_EUNSUPPORTED, "block_size %d not built (8, 16, 32)", block_size);
+        }
     }
+}
+
+// One query head per workgroup (any G), then the partition merge in split mode.
+template <bool PAGED>
+int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
+                      int32_t grid_parts, hipStream_t stream) {
+    int rc;
+#define PKV_HD(E)                                                                                 \
+    switch (head_dim) {                                                                           \
+    case 64: rc = dispatch_block<E, 64, PAGED>(p, block_size, num_seqs, grid_parts, stream); break;   \
+    case 128: rc = dispatch_block<E, 128, PAGED>(p, block_size, num_seqs, grid_parts, stream); break; \
+    default: return fail(PKV_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);          \
+    }
+    switch (dtype) {
+    case PKV_F32: PKV_HD(F32) break;
+    case PKV_F16: PKV_HD(F16) break;
+    case PKV_BF16: PKV_HD(BF16) break;
+    default: return fail(PKV_EINVAL, "bad dtype %d", dtype);
+    }
+#undef PKV_HD
+    if (rc || p.partition_size == 0) return rc;
+    return launch_reduce(p, dtype, head_dim, num_seqs, stream);
 }
 
 template <bool PAGED>
 int dispatch(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
-             int32_t grid_parts, hipStream_t stream) {
-#define PKV_HD(E)                                                                            \
-    switch (head_dim) {                                                                      \
-    case 64: return dispatch_block<E, 64, PAGED>(p, block_size, num_seqs, grid_parts, stream);   \
-    case 128: return dispatch_block<E, 128, PAGED>(p, block_size, num_seqs, grid_parts, stream); \
-    default: return fail(PKV_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);     \
-    }
-    switch (dtype) {
-    case PKV_F32: PKV_HD(F32)
-    case PKV_F16: PKV_HD(F16)
-    case PKV_BF16: PKV_HD(BF16)
-    default: return fail(PKV_EINVAL, "bad dtype %d", dtype);
-    }
-#undef PKV_HD
+             int32_t grid_parts, uint32_t flags, hipStream_t stream) {
+    if (p.group > 1 && !(flags & PKV_FLAG_SCALAR_GQA) && gqa_mfma_supported(dtype, head_dim, block_size, p.group))
+        return launch_gqa_mfma(p, dtype, block_size, PAGED, num_seqs, grid_parts, stream);
+    return dispatch_per_head<PAGED>(p, dtype, head_dim, block_size, num_seqs, grid_parts, stream);
 }
 
 // Checks shared by the paged and contiguous entry points.
@@ -523,6 +402,22 @@ AttnParams make_params(void *out, const void *q, const void *k, const void *v, c
 }
 
 }  // namespace
+
+int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t num_seqs, hipStream_t stream) {
+#define PKV_RED(E, D) hipLaunchKernelGGL((attn_reduce_kernel<E, D>), dim3(p.num_q_heads, num_seqs), dim3(D), 0, stream, p)
+    switch (dtype * 1000 + head_dim) {
+    case PKV_F32 * 1000 + 64: PKV_RED(F32, 64); break;
+    case PKV_F32 * 1000 + 128: PKV_RED(F32, 128); break;
+    case PKV_F16 * 1000 + 64: PKV_RED(F16, 64); break;
+    case PKV_F16 * 1000 + 128: PKV_RED(F16, 128); break;
+    case PKV_BF16 * 1000 + 64: PKV_RED(BF16, 64); break;
+    case PKV_BF16 * 1000 + 128: PKV_RED(BF16, 128); break;
+    default: return fail(PKV_EUNSUPPORTED, "reduce: dtype %d head_dim %d not built", dtype, head_dim);
+    }
+#undef PKV_RED
+    return hip_status(hipGetLastError(), "attention reduce launch");
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -553,15 +448,14 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (!block_tables || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "%s: block_tables NULL or max_blocks_per_seq / num_blocks not positive", fn);
     if (num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: num_blocks %lld exceeds int32", fn, (long long)num_blocks);
-    (void)flags;
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
     AttnParams p = make_params(out, q, k_cache, v_cache, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
                                partition_size, max_context_len, static_cast<int32_t>(cap), workspace);
     p.tables = block_tables;
     p.max_blocks = max_blocks_per_seq;
-    p.num_blocks = num_blocks;
+    p.num_blocks = static_cast<uint32_t>(num_blocks);
     const int32_t grid_parts = p.partition_size ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
-    return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, stream);
+    return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, flags, stream);
 }
 
 extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, const void *v, int32_t lmax,
@@ -578,11 +472,10 @@ extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const v
     // tile rows of the contiguous slab: 16 (any multiple of rows-per-load works)
     constexpr int32_t kTile = 16;
     if (partition_size % kTile) return fail(PKV_EINVAL, "%s: partition_size must be a multiple of 16", fn);
-    (void)flags;
     const int32_t cap = std::min(max_context_len, lmax);
     AttnParams p = make_params(out, q, k, v, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
                                partition_size, max_context_len, cap, workspace);
     p.lmax = lmax;
     const int32_t grid_parts = p.partition_size ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
-    return dispatch<false>(p, dtype, head_dim, kTile, num_seqs, grid_parts, stream);
+    return dispatch<false>(p, dtype, head_dim, kTile, num_seqs, grid_parts, flags, stream);
 }

@@ -1,0 +1,364 @@
+// Grouped-query decode attention on the matrix cores: the G query heads that share one
+// KV head are served by one workgroup, so each K/V tile is read from HBM once, and both
+// contractions run on MFMA.
+//
+// Same result as the one-head-per-workgroup kernel: single-query scaled dot-product attention
+// of each query head over its sequence's keys and values, gathered block by block through the
+// block table ("vLLM and PagedAttention" slide 9 and slide 10). Query head h reads KV head
+// h / G.
+//
+// Work unit: a tile of 16 consecutive rows (tokens) of one (block, kv head). With lane l,
+// g = l / 16, n = l % 16:
+//  * logits: S^T[token][head] = K[token][:] . Q^T[:][head] as 4 v_mfma_f32_16x16x32 over d.
+//    Lane l supplies K row n, 16-byte chunk 4*kk + g (the A operand) and query head n, the same
+//    chunk (the B operand; heads >= G are zero), and receives the logits of head n for tokens
+//    4g .. 4g+3 of the tile;
+//  * weighted sum: O^T[d][head] = V^T[d][token] . P^T[token][head] as 8 v_mfma_f32_16x16x16,
+//    MFMA j covering d = 8m + j (m = 0..15). Lane l's P^T operand is its own 4 softmax
+//    weights (head n, tokens 4g .. 4g+3) and its V^T operand is element j of its own 4 V loads
+//    (rows 4g .. 4g+3, chunk n), packed in pairs with v_perm: no value crosses lanes between
+//    the two contractions;
+//  * the output tile leaves head n and d = 8(4g + i) + j in lane l, so the online-softmax
+//    rescale of a head is lane-local; only the running max crosses the four lane groups, and
+//    the rescale is skipped when no head's max moved.
+// The softmax weights enter the second MFMA rounded to the input type (the sum l is taken over
+// the same rounded weights, so the output is an exact convex combination of them).
+// Loads, table handling, double buffering, masking and the split workspace are as in the
+// one-head kernel. The grid is (kv heads, partitions, sequences) with the kv head fastest, so a
+// kv head's workgroups land on the same XCDs and a shared prefix stays in their L2.
+#include "attention.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGqaWaves = 4;
+constexpr int kGqaTiles = 1;  // tiles per stage
+constexpr int kMaxGroup = 16;
+
+template <class E>
+struct Mfma;
+
+template <>
+struct Mfma<F16> {
+    static __device__ inline f32x4 mma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    }
+    static __device__ inline f32x4 mma16(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                     0, 0);
+    }
+    static __device__ inline unsigned short bits(float x) {
+        const _Float16 h = static_cast<_Float16>(x);  // round to nearest even
+        return __builtin_bit_cast(unsigned short, h);
+    }
+    static __device__ inline float value(unsigned short b) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, b));
+    }
+};
+
+template <>
+struct Mfma<BF16> {
+    static __device__ inline f32x4 mma(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       c, 0, 0, 0);
+    }
+    static __device__ inline f32x4 mma16(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                         0, 0, 0);
+    }
+    static __device__ inline unsigned short bits(float x) {
+        const __bf16 h = static_cast<__bf16>(x);  // round to nearest even
+        return __builtin_bit_cast(unsigned short, h);
+    }
+    static __device__ inline float value(unsigned short b) { return __uint_as_float(static_cast<unsigned>(b) << 16); }
+};
+
+__device__ inline unsigned word(const u32x4 &r, int w) {
+    return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
+}
+
+// Grid = (num_kv_heads, parts, num_seqs), block = 64 * W. head_dim 128, 16-bit types.
+// U tiles per stage; stages are double-buffered in registers.
+template <class E, int B, bool PAGED, int W, int U>
+__global__ __launch_bounds__(W * 64) void attn_gqa_mfma_kernel(const AttnParams p) {
+    using M = Mfma<E>;
+    constexpr int D = 128;
+    constexpr int TR = 16;          // tile rows
+    constexpr int SPB = B / TR;     // tiles per block
+    constexpr int ROWB = D * 2;     // bytes per row
+    static_assert(B % TR == 0, "block_size must be a multiple of 16");
+    static_assert(64 % U == 0, "a stage must not straddle a table chunk");
+
+    __shared__ float s_m[W][kMaxGroup], s_l[W][kMaxGroup];
+    __shared__ float s_acc[W][kMaxGroup][D];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
+    const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
+    const int G = p.group;
+    const int n = lane & 15, g = lane >> 4;
+    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
+    const int jt0 = t0 / TR;
+    const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+
+    const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
+    int tb = 0;
+    auto fetch_table = [&](int base) -> int {
+        const int j = (jt0 + wave + (base + lane) * W) / SPB;
+        return j < p.max_blocks ? trow[j] : 0;
+    };
+    if constexpr (PAGED) tb = fetch_table(0);
+
+    // Q^T operand: query head n of the group, chunks 4*kk + g; zero for n >= G.
+    u32x4 qv[4];
+    {
+        const char *qp = static_cast<const char *>(p.q) + ((row_q0 + n) * D + g * 8) * 2;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qv[kk] = n < G ? *reinterpret_cast<const u32x4 *>(qp + kk * 64) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
+    if (t0 >= t1) {
+        if (p.partition_size == 0)
+            for (int i = threadIdx.x; i < G * D; i += W * 64) E::store(p.out, row_q0 * D + i, 0.f);
+        return;
+    }
+
+    const char *kc = static_cast<const char *>(p.k);
+    const char *vc = static_cast<const char *>(p.v);
+    const int ntile = (t1 + TR - 1) / TR - jt0;
+    const int nk = ntile > wave ? (ntile - wave + W - 1) / W : 0;
+
+    auto tile_offset = [&](int k, int kc0, bool &ok) -> int64_t {
+        const int jt = jt0 + wave + k * W;
+        if constexpr (PAGED) {
+            const int pb = __builtin_amdgcn_readlane(tb, k - kc0);
+            ok = static_cast<uint32_t>(pb) < p.num_blocks;  // 32-bit, so it stays a scalar compare
+            const int64_t blk = ok ? pb : 0;
+            return ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
+        } else {
+            ok = true;
+            return ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
+        }
+    };
+
+    struct Stage {
+        u32x4 k[U][4], v[U][4];
+        int tok0[U];
+        bool ok[U];  // table entry inside the pool
+        bool in[U];  // tile belongs to this wave (false: a stand-in, masked out)
+    };
+
+    // Every load is unconditional (exact wait counts). With clamp set, a tile past the wave's
+    // last is replaced by its last tile and a row at or past t1 by the row before t1: in bounds
+    // and written; consume() masks them out.
+    auto issue = [&](Stage &S, int kc0, int st, bool clamp) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int k = kc0 + st * U + u;
+            S.in[u] = k < nk;
+            if (clamp) k = min(k, nk - 1);
+            const int64_t tile = tile_offset(k, kc0, S.ok[u]);
+            const char *kt = kc + tile, *vt = vc + tile;
+            S.tok0[u] = (jt0 + wave + k * W) * TR;
+            const int lim = t1 - 1 - S.tok0[u];
+            const unsigned krow = clamp ? min(n, lim) : n;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) S.k[u][kk] = nt_load(kt + (krow * ROWB + (4 * kk + g) * 16));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const unsigned vrow = clamp ? min(4 * g + i, lim) : 4 * g + i;
+                S.v[u][i] = nt_load(vt + (vrow * ROWB + n * 16));
+            }
+        }
+    };
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto consume = [&](Stage &S, bool tail) {
+        float sc[U][4];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[u][kk], qv[kk], c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = S.ok[u] && (!tail || (S.in[u] && S.tok0[u] + 4 * g + i < t1));
+                sc[u][i] = valid ? c[i] * p.scale_log2 : -INFINITY;
+                mloc = fmaxf(mloc, sc[u][i]);
+            }
+        }
+        // the head's running max over all four lane groups
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m, mloc);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        // rescale only when some head's max moved (uniform branch; alpha = 1 elsewhere)
+        if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+            const float alpha = fast_exp2(m - m_ref);
+            lsum *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // P^T operand: head n, tokens 4g .. 4g+3 of tile u
+            unsigned short pb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pb[i] = M::bits(fast_exp2(sc[u][i] - m_ref));
+                lsum += M::value(pb[i]);
+            }
+            const u32x2 pt = {static_cast<unsigned>(pb[0]) | (static_cast<unsigned>(pb[1]) << 16),
+                              static_cast<unsigned>(pb[2]) | (static_cast<unsigned>(pb[3]) << 16)};
+            // a rejected table entry's tile was read from a clamped block (its values may not be
+            // finite) and a stand-in tile adds nothing: neither enters the weighted sum
+            if (!S.ok[u] || (tail && !S.in[u])) continue;
+            // V^T operand of MFMA j: element j of the lane's 4 V rows
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int w = j >> 1;
+                const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[u][1], w), word(S.v[u][0], w), sel),
+                                  __builtin_amdgcn_perm(word(S.v[u][3], w), word(S.v[u][2], w), sel)};
+                acc[j] = M::mma16(vt, pt, acc[j]);
+            }
+        }
+        m = m_new;
+    };
+
+    // The wave's tiles in chunks of 64 (one table register each); stages of U tiles are
+    // double-buffered; only a wave's last stages need clamping and masks.
+    for (int kc0 = 0; kc0 < nk; kc0 += 64) {
+        if constexpr (PAGED) {
+            if (kc0 > 0) tb = fetch_table(kc0);
+        }
+        const int nst = (min(64, nk - kc0) + U - 1) / U;
+        const bool last_chunk = kc0 + 64 >= nk;
+        Stage A, Bs;
+        int st = 0;
+        issue(A, kc0, 0, last_chunk && nst < 2);
+        while (st + 4 <= nst) {
+            issue(Bs, kc0, st + 1, false);
+            consume(A, false);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(A, kc0, st + 2, false);
+            consume(Bs, false);
+            __builtin_amdgcn_sched_barrier(0);
+            st += 2;
+        }
+        switch (nst - st) {
+        case 1:
+            consume(A, true);
+            break;
+        case 2:
+            issue(Bs, kc0, st + 1, true);
+            consume(A, true);
+            consume(Bs, true);
+            break;
+        default:
+            issue(Bs, kc0, st + 1, true);
+            consume(A, true);
+            issue(A, kc0, st + 2, true);
+            consume(Bs, true);
+            consume(A, true);
+            break;
+        }
+    }
+
+    // the head's weight sum over the four lane groups (each holds its own tokens' share)
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (n < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s_acc[wave][n][8 * (4 * g + i) + j] = acc[j][i];
+        if (g == 0) {
+            s_m[wave][n] = m;
+            s_l[wave][n] = lsum;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += W * 64) {
+        const int h = idx / D, dd = idx % D;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+        const float Mr = Mx == -INFINITY ? 0.f : Mx;
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = fast_exp2(s_m[w][h] - Mr);
+            L = fmaf(s_l[w][h], f, L);
+            O = fmaf(s_acc[w][h][dd], f, O);
+        }
+        const int64_t row_q = row_q0 + h;
+        if (p.partition_size > 0) {
+            const int64_t wr = row_q * p.num_parts + part;
+            p.ws[wr * D + dd] = O;
+            if (dd == 0) {
+                p.ws[p.ws_rows * D + wr] = Mx;
+                p.ws[p.ws_rows * (D + 1) + wr] = L;
+            }
+        } else {
+            E::store(p.out, row_q * D + dd, L > 0.f ? O / L : 0.f);
+        }
+    }
+}
+
+template <class E, int B, bool PAGED>
+int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>), dim3(p.num_kv_heads, grid_parts, num_seqs),
+                       dim3(kGqaWaves * 64), 0, stream, p);
+    return hip_status(hipGetLastError(), "grouped-query attention launch");
+}
+
+template <class E, bool PAGED>
+int launch_block(const AttnParams &p, int32_t block_size, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
+    if constexpr (!PAGED) {
+        return launch_one<E, 16, false>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+    } else {
+        return block_size == 32 ? launch_one<E, 32, true>(p, num_seqs, grid_parts, stream)
+                                : launch_one<E, 16, true>(p, num_seqs, grid_parts, stream);
+    }
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
+    return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && (block_size == 16 || block_size == 32) &&
+           group >= 2 && group <= kMaxGroup;
+}
+
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int32_t num_seqs,
+                    int32_t grid_parts, hipStream_t stream) {
+    if (p.num_kv_heads > 65535 || grid_parts > 65535)
+        return fail(PKV_EINVAL, "grouped-query attention: %d kv heads x %d partitions exceed the grid", p.num_kv_heads,
+                    grid_parts);
+    int rc;
+    if (dtype == PKV_F16)
+        rc = paged ? launch_block<F16, true>(p, block_size, num_seqs, grid_parts, stream)
+                   : launch_block<F16, false>(p, block_size, num_seqs, grid_parts, stream);
+    else
+        rc = paged ? launch_block<BF16, true>(p, block_size, num_seqs, grid_parts, stream)
+                   : launch_block<BF16, false>(p, block_size, num_seqs, grid_parts, stream);
+    if (rc || p.partition_size == 0) return rc;
+    return launch_reduce(p, dtype, 128, num_seqs, stream);
+}
+
+}  // namespace pkv

@@ -34,6 +34,13 @@ SMALL = {
                                                         d=64, dtype="f16", partition_size=256),
     "gqa-small-g8-fp32": lambda: synth.gqa_shared_prefix(num_seqs=4, prefix=32, median=80, cap=500, hq=16, hkv=2,
                                                          d=64, dtype="f32", partition_size=128),
+    # matrix-core grouped-query kernel: f16 and bf16, G = 2, 8, 16, block sizes 16 and 32
+    "gqa-small-f16-g8-b32": lambda: synth.gqa_shared_prefix(num_seqs=5, prefix=48, median=150, cap=700, hq=16, hkv=2,
+                                                            d=128, block_size=32, dtype="f16", partition_size=256),
+    "gqa-small-bf16-g2": lambda: synth.gqa_shared_prefix(num_seqs=6, prefix=40, median=120, cap=600, hq=8, hkv=4,
+                                                         d=128, dtype="bf16", partition_size=128),
+    "gqa-small-bf16-g16": lambda: synth.gqa_shared_prefix(num_seqs=3, prefix=32, median=100, cap=400, hq=16, hkv=1,
+                                                          d=128, dtype="bf16", partition_size=128),
 }
 FULL = {
     "13b": lambda: synth.llama13b(),
@@ -291,3 +298,16 @@ def test_cow_sampling_step_by_step(full):
     if steps:
         assert n_copies[-steps] == int(np.minimum((priv > 0).sum(axis=1), priv.shape[1] - 1).sum())
         assert sum(n_copies[-steps + 1:]) == 0
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,B", [("f16", 2, 2, 8), ("bf16", 8, 2, 16), ("f16", 4, 1, 32)])
+def test_long_context_spans_table_chunks(dtype, hq, hkv, B):
+    """Contexts long enough that a wave walks more than 64 tiles, so its block-table register is
+    refilled: single pass and split, against the oracle."""
+    w = synth.decode_workload("long", 31, [9000, 8300, 40], hq, hkv, 128, B, dtype, 0.5, 0.5)
+    say(f"[long {dtype} Hq={hq} Hkv={hkv} B={B}] blocks={w.num_blocks}")
+    st = oracle.replay(w)
+    ref = oracle.attention_of(st, w)
+    c = gpu_replay(w)
+    for P in (0, 1024):
+        assert_close(gpu_attention(c, w, partition_size=P), ref, dtype, f"long P={P}")
