@@ -85,9 +85,11 @@ __device__ inline unsigned word(const u32x4 &r, int w) {
 }
 
 // Grid = (num_kv_heads, parts, num_seqs), block = 64 * W. head_dim 128, 16-bit types.
-// U tiles per stage; stages are double-buffered in registers.
+// U tiles per stage; stages are double-buffered in registers. At most 256 registers per lane
+// (two waves per SIMD), so two workgroups share a CU and one's start-up hides behind the other.
 template <class E, int B, bool PAGED, int W, int U>
-__global__ __launch_bounds__(W * 64) void attn_gqa_mfma_kernel(const AttnParams p) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
+    const AttnParams p) {
     using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;          // tile rows
