@@ -57,6 +57,11 @@ typedef enum pkv_dtype {
 /* Attention flags. */
 #define PKV_FLAG_SCALAR_GQA 1u /* use the one-query-head-per-workgroup kernel even when G > 1 */
 
+/* partition_size value for the balanced split: the library cuts the whole batch's work into
+ * equal shares, one per workgroup on the device (a (sequence, head) may be cut anywhere), and a
+ * merge pass combines the rows cut between shares. Up to 4096 sequences. */
+#define PKV_PARTITION_BALANCED (-1)
+
 const char *pkv_last_error(void);
 const char *pkv_version(void);
 
@@ -148,9 +153,11 @@ int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride
 int pkv_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers, int64_t num_blocks,
                     int64_t block_bytes, const int32_t *pairs, int32_t num_pairs, hipStream_t stream);
 
-/* Bytes of fp32 workspace the split-partition mode needs:
- * num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4.
- * 0 when partition_size == 0. */
+/* Bytes of fp32 workspace a split mode needs:
+ *  partition_size > 0: num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4;
+ *  PKV_PARTITION_BALANCED: 2 * (2 * the current device's compute units) * num_q_heads * (head_dim + 2) * 4
+ *                          (0 if the device cannot be queried);
+ *  partition_size == 0: 0. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);
 
@@ -167,6 +174,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *  partition_size: 0 = one pass per (sequence, head). > 0 (a multiple of block_size):
  *                 each (sequence, head) is cut into parts of that many tokens, computed
  *                 independently into workspace, then merged by a log-sum-exp reduce pass.
+ *                 PKV_PARTITION_BALANCED: the batch's tiles are shared out evenly (see above),
+ *                 then the same kind of merge; rounding then depends on the device's
+ *                 compute-unit count (results are still reproducible on one device).
  *  workspace:     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned;
  *                 may be NULL when partition_size == 0.
  *  flags:         PKV_FLAG_SCALAR_GQA or 0.

@@ -15,6 +15,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline float as_f(unsigned u) { return __uint_as_float(u); }
 
 struct F32 {
+    static constexpr int CODE = PKV_F32;
     static constexpr int VEC = 4;
     static constexpr int ELT = 4;
     static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
@@ -33,6 +34,7 @@ struct F32 {
 };
 
 struct F16 {
+    static constexpr int CODE = PKV_F16;
     static constexpr int VEC = 8;
     static constexpr int ELT = 2;
     static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
@@ -56,6 +58,7 @@ struct F16 {
 };
 
 struct BF16 {
+    static constexpr int CODE = PKV_BF16;
     static constexpr int VEC = 8;
     static constexpr int ELT = 2;
     static __device__ inline float dot(const u32x4 &q, const u32x4 &k, float a) {
@@ -95,14 +98,111 @@ struct AttnParams {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;         // num_q_heads / num_kv_heads
-    int32_t partition_size;  // 0 = single pass
+    int32_t partition_size;  // 0 = single pass, > 0 = fixed partitions, PKV_PARTITION_BALANCED
     int32_t num_parts;       // workspace parts per (sequence, head)
     float scale_log2;        // scale * log2(e)
+    int32_t num_seqs;
+    int32_t head_dim;
+    size_t ws_bytes;
+    int32_t balanced_wgs;    // balanced schedule: workgroups sharing the batch's tiles
+    int32_t tile_rows;       // balanced schedule: rows (tokens) per tile
+    int32_t rows_per_seq;    // balanced schedule: work rows per sequence (query heads, or kv heads)
+    int32_t heads_per_row;   // balanced schedule: query heads one work row serves
+};
+
+// Where a workgroup's merged result for one work row goes: acc == nullptr means the final,
+// normalised output in the element type; otherwise the unnormalised accumulator, the running
+// max m and the sum l of each head (head j at acc + j*acc_stride, m + j*ml_stride, l + ...).
+struct Sink {
+    float *acc;
+    float *m;
+    float *l;
+    int64_t acc_stride;
+    int64_t ml_stride;
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+// ---------------------------------------------------------------- balanced schedule
+// The work rows of the batch, sequence by sequence, each cut into tiles of tile_rows tokens,
+// form one list of T tiles; workgroup g takes tiles [b(g), b(g+1)), b(g) = floor(g*T/W). A row
+// that one workgroup holds whole is written to the output; a row cut between workgroups leaves
+// one partial result per workgroup in the workspace (slot 2g for the workgroup's first row,
+// 2g+1 for its last), merged in workgroup order by attn_reduce_balanced_kernel.
+constexpr int kBalancedMaxSeqs = 4096;
+constexpr int kBalancedWgsPerCu = 2;
+
+__device__ inline int64_t balanced_begin(int64_t g, int64_t T, int64_t nwg) { return g * T / nwg; }
+
+// The workgroup whose range holds tile x (0 <= x < T).
+__device__ inline int64_t balanced_owner(int64_t x, int64_t T, int64_t nwg) { return ((x + 1) * nwg - 1) / T; }
+
+// C[s] = tiles per row of the sequences before s, for s = 0 .. S (LDS, all threads of the
+// block); lengths clamped as everywhere else. Ends with a barrier.
+template <int NT>
+__device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_t *part) {
+    const int t = threadIdx.x, S = p.num_seqs, TR = p.tile_rows;
+    const int per = (S + NT - 1) / NT, s0 = t * per;
+    uint32_t sum = 0;
+    for (int i = 0; i < per; ++i)
+        if (s0 + i < S) sum += (clamp_ctx(p.ctx_lens[s0 + i], p.ctx_cap) + TR - 1) / TR;
+    part[t] = sum;
+    __syncthreads();
+    for (int o = 1; o < NT; o <<= 1) {
+        const uint32_t v = t >= o ? part[t - o] : 0u;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    uint32_t run = t > 0 ? part[t - 1] : 0u;
+    for (int i = 0; i < per; ++i)
+        if (s0 + i < S) {
+            C[s0 + i] = run;
+            run += (clamp_ctx(p.ctx_lens[s0 + i], p.ctx_cap) + TR - 1) / TR;
+        }
+    if (t == NT - 1) C[S] = part[NT - 1];
+    __syncthreads();
+}
+
+// Walk this workgroup's share of the balanced list: body(s, row, tile_begin, tile_end, sink)
+// for each row segment, in order. Uniform over the workgroup.
+template <int D, class Body>
+__device__ inline void balanced_walk(const AttnParams &p, const uint32_t *C, Body &&body) {
+    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, g = blockIdx.x;
+    const int64_t T = R * C[p.num_seqs];
+    if (T == 0) return;
+    int64_t pos = balanced_begin(g, T, nwg);
+    const int64_t end = balanced_begin(g + 1, T, nwg);
+    if (pos >= end) return;
+    int lo = 0, hi = p.num_seqs;  // largest s with R*C[s] <= pos (it has tiles: R*C[s+1] > pos)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (R * C[mid] <= pos) lo = mid; else hi = mid;
+    }
+    int s = lo;
+    bool first = true;
+    const int64_t slot_floats = static_cast<int64_t>(p.heads_per_row) * (D + 2);
+    while (pos < end) {
+        const int64_t n = C[s + 1] - C[s], base = R * C[s];
+        const int row = static_cast<int>((pos - base) / n);
+        const int64_t row0 = base + row * n;
+        const int ta = static_cast<int>(pos - row0);
+        const int tb = static_cast<int>(end - row0 < n ? end - row0 : n);
+        Sink sink{nullptr, nullptr, nullptr, 0, 0};
+        if (ta != 0 || tb != n) {
+            float *slot = p.ws + (2 * g + (first ? 0 : 1)) * slot_floats;
+            sink = Sink{slot, slot + p.heads_per_row * D, slot + p.heads_per_row * (D + 1), D, 1};
+        }
+        body(s, row, ta, tb, sink);
+        first = false;
+        pos = row0 + tb;
+        if (pos == base + R * n)  // past the sequence's last row: next sequence with tiles
+            do ++s; while (s < p.num_seqs && C[s + 1] == C[s]);
+    }
+}
+
 
 // DPP lane moves within a row of 16 lanes.
 constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
@@ -143,5 +243,12 @@ int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool
                     int32_t grid_parts, hipStream_t stream);
 // The partition merge (attention.hip), shared by both kernels.
 int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t num_seqs, hipStream_t stream);
+// The balanced schedule's merge of cut rows (attention.hip).
+int launch_reduce_balanced(const AttnParams &p, int32_t dtype, int32_t head_dim, hipStream_t stream);
+// Compute units of the current device (cached), or -1.
+int device_compute_units();
+// Sets p.balanced_wgs and checks the balanced schedule's limits and workspace (p.tile_rows and
+// p.heads_per_row set by the caller).
+int balanced_check(AttnParams &p);
 
 }  // namespace pkv

@@ -33,6 +33,7 @@
 // The contiguous-cache variant is the same template; only a tile's address
 // differs.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "attention.h"
@@ -58,31 +59,34 @@ struct Shape {
     static_assert(64 % U == 0, "a stage must not straddle a table chunk");
 };
 
-// Main kernel: grid = (parts, num_q_heads, num_seqs), block = 64 * W.
+template <int W, int D>
+struct MhaLds {
+    float m[W], l[W];
+    float acc[W][D];
+};
+
+// Tokens [t0, t1) of sequence s for query head h (t0 a multiple of the tile rows, t0 < t1 <= the
+// length): the workgroup's merged result goes to sink. Uniform over the workgroup; ends with a
+// barrier, so the caller may run it again on the same LDS.
 template <class E, int D, int B, bool PAGED, int W>
-__global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
+__device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int t1, const Sink &sink,
+                                 MhaLds<W, D> &lds) {
     using SH = Shape<E, D, B>;
     constexpr int VEC = SH::VEC, LPR = SH::LPR, RPI = SH::RPI, TR = SH::TR, SPB = SH::SPB, NL = SH::NL,
                   U = SH::U;
 
-    __shared__ float s_m[W], s_l[W];
-    __shared__ float s_acc[W][D];
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
-    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
     const int kvh = h / p.group;
     const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
     const int r0 = lane / LPR, c = lane % LPR;
-    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
 
     // Tiles of this workgroup: jt0 .. jt0+n-1 (tile jt covers tokens jt*TR .. jt*TR+TR-1);
     // this wave takes tiles jt0 + wave + k*W, k = 0 .. nk-1, in stages of U tiles.
     const int jt0 = t0 / TR;
 
-    // Block-table chunk: lane i holds the physical block of this wave's tile kb + i. The
-    // first chunk is requested together with the length and the query (it depends on
-    // neither); entries past the sequence's last block are read but never used.
+    // Block-table chunk: lane i holds the physical block of this wave's tile kc0 + i; entries
+    // past the sequence's last block are read but never used.
     const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
     int tb = 0;
     auto fetch_table = [&](int base) -> int {
@@ -91,14 +95,6 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     };
     if constexpr (PAGED) tb = fetch_table(0);
     const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
-
-    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
-    if (t0 >= t1) {  // uniform over the workgroup
-        if (p.partition_size == 0)
-            for (int i = threadIdx.x; i < D; i += W * 64) E::store(p.out, row_q * D + i, 0.f);
-        return;
-    }
 
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
@@ -246,36 +242,75 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
     }
     if (lane < LPR) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s_acc[wave][c * VEC + e] = acc[e];
+        for (int e = 0; e < VEC; ++e) lds.acc[wave][c * VEC + e] = acc[e];
     }
     if (lane == 0) {
-        s_m[wave] = m;
-        s_l[wave] = lsum;
+        lds.m[wave] = m;
+        lds.l[wave] = lsum;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < D; i += W * 64) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, lds.m[w]);
         const float Mr = M == -INFINITY ? 0.f : M;
         float L = 0.f, O = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float f = fast_exp2(s_m[w] - Mr);
-            L = fmaf(s_l[w], f, L);
-            O = fmaf(s_acc[w][i], f, O);
+            const float f = fast_exp2(lds.m[w] - Mr);
+            L = fmaf(lds.l[w], f, L);
+            O = fmaf(lds.acc[w][i], f, O);
         }
-        if (p.partition_size > 0) {
-            const int64_t wr = row_q * p.num_parts + part;
-            p.ws[wr * D + i] = O;
+        if (sink.acc) {
+            sink.acc[i] = O;
             if (i == 0) {
-                p.ws[p.ws_rows * D + wr] = M;
-                p.ws[p.ws_rows * (D + 1) + wr] = L;
+                sink.m[0] = M;
+                sink.l[0] = L;
             }
         } else {
             E::store(p.out, row_q * D + i, L > 0.f ? O / L : 0.f);
         }
     }
+    __syncthreads();
+}
+
+// Per-item schedule: grid = (parts, num_q_heads, num_seqs), block = 64 * W; one workgroup per
+// (sequence, query head[, partition]).
+template <class E, int D, int B, bool PAGED, int W>
+__global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
+    __shared__ MhaLds<W, D> lds;
+    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
+    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
+    if (t0 >= t1) {  // uniform over the workgroup
+        if (p.partition_size == 0)
+            for (int i = threadIdx.x; i < D; i += W * 64) E::store(p.out, row_q * D + i, 0.f);
+        return;
+    }
+    Sink sink{nullptr, nullptr, nullptr, 0, 0};
+    if (p.partition_size > 0) {
+        const int64_t wr = row_q * p.num_parts + part;
+        sink = Sink{p.ws + wr * D, p.ws + p.ws_rows * D + wr, p.ws + p.ws_rows * (D + 1) + wr, 0, 0};
+    }
+    mha_range<E, D, B, PAGED, W>(p, s, h, t0, t1, sink, lds);
+}
+
+// Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
+// (work rows = (sequence, query head)); cut rows are merged by attn_reduce_balanced_kernel.
+template <class E, int D, int B, bool PAGED, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_balanced_kernel(
+    const AttnParams p) {
+    __shared__ MhaLds<W, D> lds;
+    __shared__ uint32_t C[kBalancedMaxSeqs + 1];
+    __shared__ uint32_t part[W * 64];
+    balanced_prefix<W * 64>(p, C, part);
+    balanced_walk<D>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
+        constexpr int TR = Shape<E, D, B>::TR;
+        const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+        mha_range<E, D, B, PAGED, W>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
+    });
 }
 
 // Merge of the partitions of one (sequence, head): grid = (num_q_heads, num_seqs), block = D.
@@ -300,11 +335,87 @@ __global__ __launch_bounds__(D) void attn_reduce_kernel(const AttnParams p) {
     E::store(p.out, row_q * D + i, L > 0.f ? O / L : 0.f);
 }
 
+// The balanced schedule's merge: grid = (rows_per_seq, num_seqs), block = 256. A row with no
+// tiles gets zeros; a row one workgroup held whole was written by it; a cut row's partial results
+// (one per workgroup that held part of it) are merged here in workgroup order.
+template <class E, int D>
+__global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnParams p) {
+    __shared__ uint32_t red[2][256];
+    const int row = blockIdx.x, s = blockIdx.y, t = threadIdx.x, TR = p.tile_rows;
+    uint32_t before = 0, all = 0;
+    for (int i = t; i < p.num_seqs; i += 256) {
+        const uint32_t n = (clamp_ctx(p.ctx_lens[i], p.ctx_cap) + TR - 1) / TR;
+        all += n;
+        if (i < s) before += n;
+    }
+    red[0][t] = before;
+    red[1][t] = all;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (t < o) {
+            red[0][t] += red[0][t + o];
+            red[1][t] += red[1][t + o];
+        }
+        __syncthreads();
+    }
+    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, T = R * red[1][0];
+    const int64_t n = (clamp_ctx(p.ctx_lens[s], p.ctx_cap) + TR - 1) / TR;
+    const int H = p.heads_per_row;
+    const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(row) * H;
+    if (n == 0) {
+        for (int i = t; i < H * D; i += 256) E::store(p.out, row_q0 * D + i, 0.f);
+        return;
+    }
+    const int64_t row0 = R * red[0][0] + row * n;
+    const int64_t g0 = balanced_owner(row0, T, nwg), g1 = balanced_owner(row0 + n - 1, T, nwg);
+    if (g0 == g1) return;
+    const int64_t slot_floats = static_cast<int64_t>(H) * (D + 2);
+    // the first owner's part of this row is its first row only if its range starts on the row
+    const int64_t first_slot = balanced_begin(g0, T, nwg) < row0 ? 2 * g0 + 1 : 2 * g0;
+    // workgroups with an empty range (more workgroups than tiles) hold nothing and are skipped
+    auto empty = [&](int64_t g) { return balanced_begin(g + 1, T, nwg) == balanced_begin(g, T, nwg); };
+    for (int i = t; i < H * D; i += 256) {
+        const int j = i / D, d = i % D;
+        float M = -INFINITY;
+        for (int64_t g = g0; g <= g1; ++g) {
+            if (empty(g)) continue;
+            const float *slot = p.ws + (g == g0 ? first_slot : 2 * g) * slot_floats;
+            M = fmaxf(M, slot[H * D + j]);
+        }
+        const float Mr = M == -INFINITY ? 0.f : M;
+        float L = 0.f, O = 0.f;
+        for (int64_t g = g0; g <= g1; ++g) {
+            if (empty(g)) continue;
+            const float *slot = p.ws + (g == g0 ? first_slot : 2 * g) * slot_floats;
+            const float f = fast_exp2(slot[H * D + j] - Mr);
+            L = fmaf(slot[H * (D + 1) + j], f, L);
+            O = fmaf(slot[j * D + d], f, O);
+        }
+        E::store(p.out, (row_q0 + j) * D + d, L > 0.f ? O / L : 0.f);
+    }
+}
+
+constexpr int kBalancedWaves = 4;
+
 template <class E, int D, int B, bool PAGED>
 int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
+    if (p.partition_size == PKV_PARTITION_BALANCED) {
+        AttnParams q = p;
+        q.tile_rows = Shape<E, D, B>::TR;
+        q.rows_per_seq = p.num_q_heads;
+        q.heads_per_row = 1;
+        int rc = balanced_check(q);
+        if (rc) return rc;
+        hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves>), dim3(q.balanced_wgs),
+                           dim3(kBalancedWaves * 64), 0, stream, q);
+        rc = hip_status(hipGetLastError(), "attention launch");
+        return rc ? rc : launch_reduce_balanced(q, E::CODE, D, stream);
+    }
     hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves>), dim3(grid_parts, p.num_q_heads, num_seqs),
                        dim3(kThreads), 0, stream, p);
-    return hip_status(hipGetLastError(), "attention launch");
+    int rc = hip_status(hipGetLastError(), "attention launch");
+    if (rc || p.partition_size <= 0) return rc;
+    return launch_reduce(p, E::CODE, D, num_seqs, stream);
 }
 
 template <class E, int D, bool PAGED>
@@ -322,7 +433,7 @@ int dispatch_block(const AttnParams &p, int32_t block_size, int32_t num_seqs, in
     }
 }
 
-// One query head per workgroup (any G), then the partition merge in split mode.
+// One query head per workgroup (any G), then the merge pass of the split modes.
 template <bool PAGED>
 int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
                       int32_t grid_parts, hipStream_t stream) {
@@ -340,8 +451,7 @@ int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int3
     default: return fail(PKV_EINVAL, "bad dtype %d", dtype);
     }
 #undef PKV_HD
-    if (rc || p.partition_size == 0) return rc;
-    return launch_reduce(p, dtype, head_dim, num_seqs, stream);
+    return rc;
 }
 
 template <bool PAGED>
@@ -366,12 +476,14 @@ int check_common(const char *fn, const void *out, const void *q, const void *k, 
         return fail(PKV_EUNSUPPORTED, "%s: head_dim %d not built (64, 128)", fn, head_dim);
     if (max_context_len < 0) return fail(PKV_EINVAL, "%s: max_context_len < 0", fn);
     if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
-    if (partition_size < 0) return fail(PKV_EINVAL, "%s: partition_size < 0", fn);
+    if (partition_size < 0 && partition_size != PKV_PARTITION_BALANCED)
+        return fail(PKV_EINVAL, "%s: partition_size %d (0, > 0, or PKV_PARTITION_BALANCED)", fn, partition_size);
     if (num_seqs == 0) return PKV_OK;
     if (!out || !q || !k || !v || !context_lens) return fail(PKV_EINVAL, "%s: NULL pointer", fn);
     if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
         return fail(PKV_EINVAL, "%s: out, q, k, v must be 16-byte aligned", fn);
-    if (partition_size > 0) {
+    if (partition_size != 0) {
+        // (the balanced mode's exact need depends on the kernel chosen; it is checked again at launch)
         const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
         if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need))
             return fail(PKV_EINVAL, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn, need,
@@ -382,7 +494,8 @@ int check_common(const char *fn, const void *out, const void *q, const void *k, 
 
 AttnParams make_params(void *out, const void *q, const void *k, const void *v, const int32_t *context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, float scale,
-                       int32_t partition_size, int32_t max_context_len, int32_t ctx_cap, void *workspace) {
+                       int32_t partition_size, int32_t max_context_len, int32_t ctx_cap, void *workspace,
+                       size_t workspace_bytes, int32_t head_dim) {
     AttnParams p{};
     p.out = out;
     p.q = q;
@@ -398,6 +511,9 @@ AttnParams make_params(void *out, const void *q, const void *k, const void *v, c
     p.num_parts = partition_size > 0 ? static_cast<int32_t>(ceil_div(max_context_len, partition_size)) : 0;
     p.ws_rows = static_cast<int64_t>(num_seqs) * num_q_heads * p.num_parts;
     p.ws = static_cast<float *>(workspace);
+    p.num_seqs = num_seqs;
+    p.head_dim = head_dim;
+    p.ws_bytes = workspace ? workspace_bytes : 0;
     return p;
 }
 
@@ -418,13 +534,64 @@ int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t 
     return hip_status(hipGetLastError(), "attention reduce launch");
 }
 
+int launch_reduce_balanced(const AttnParams &p, int32_t dtype, int32_t head_dim, hipStream_t stream) {
+#define PKV_RED(E, D) \
+    hipLaunchKernelGGL((attn_reduce_balanced_kernel<E, D>), dim3(p.rows_per_seq, p.num_seqs), dim3(256), 0, stream, p)
+    switch (dtype * 1000 + head_dim) {
+    case PKV_F32 * 1000 + 64: PKV_RED(F32, 64); break;
+    case PKV_F32 * 1000 + 128: PKV_RED(F32, 128); break;
+    case PKV_F16 * 1000 + 64: PKV_RED(F16, 64); break;
+    case PKV_F16 * 1000 + 128: PKV_RED(F16, 128); break;
+    case PKV_BF16 * 1000 + 64: PKV_RED(BF16, 64); break;
+    case PKV_BF16 * 1000 + 128: PKV_RED(BF16, 128); break;
+    default: return fail(PKV_EUNSUPPORTED, "reduce: dtype %d head_dim %d not built", dtype, head_dim);
+    }
+#undef PKV_RED
+    return hip_status(hipGetLastError(), "balanced reduce launch");
+}
+
+int device_compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int balanced_check(AttnParams &p) {
+    if (p.num_seqs > kBalancedMaxSeqs)
+        return fail(PKV_EUNSUPPORTED, "balanced partitioning: %d sequences, at most %d", p.num_seqs, kBalancedMaxSeqs);
+    const int64_t tiles = static_cast<int64_t>(p.num_seqs) * ceil_div(p.ctx_cap, p.tile_rows);
+    if (tiles >= (int64_t(1) << 31)) return fail(PKV_EINVAL, "balanced partitioning: %lld tiles per row", (long long)tiles);
+    const int cus = device_compute_units();
+    if (cus <= 0) return fail(PKV_EHIP, "balanced partitioning: cannot read the device's compute-unit count");
+    p.balanced_wgs = kBalancedWgsPerCu * cus;
+    const size_t need = static_cast<size_t>(2) * p.balanced_wgs * p.heads_per_row * (p.head_dim + 2) * sizeof(float);
+    if (!p.ws || p.ws_bytes < need)
+        return fail(PKV_EINVAL, "balanced partitioning: workspace of %zu bytes needed, %zu given", need, p.ws_bytes);
+    return PKV_OK;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
 
 extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                              int32_t max_context_len, int32_t partition_size) {
-    if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+    if (partition_size == PKV_PARTITION_BALANCED) {
+        // two partial-result slots per workgroup, each for up to num_q_heads heads
+        const int cus = device_compute_units();
+        if (cus <= 0) return 0;
+        return static_cast<size_t>(2) * kBalancedWgsPerCu * cus * num_q_heads * (head_dim + 2) * sizeof(float);
+    }
+    if (partition_size <= 0) return 0;
     const int64_t parts = ceil_div(max_context_len, partition_size);
     return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
 }
@@ -442,7 +609,7 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (rc || num_seqs == 0) return rc;
     if (block_size != 8 && block_size != 16 && block_size != 32)
         return fail(PKV_EUNSUPPORTED, "%s: block_size %d not built (8, 16, 32)", fn, block_size);
-    if (partition_size % block_size)
+    if (partition_size > 0 && partition_size % block_size)
         return fail(PKV_EINVAL, "%s: partition_size %d is not a multiple of block_size %d", fn, partition_size,
                     block_size);
     if (!block_tables || max_blocks_per_seq <= 0 || num_blocks <= 0)
@@ -450,11 +617,12 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: num_blocks %lld exceeds int32", fn, (long long)num_blocks);
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
     AttnParams p = make_params(out, q, k_cache, v_cache, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
-                               partition_size, max_context_len, static_cast<int32_t>(cap), workspace);
+                               partition_size, max_context_len, static_cast<int32_t>(cap), workspace,
+                               workspace_bytes, head_dim);
     p.tables = block_tables;
     p.max_blocks = max_blocks_per_seq;
     p.num_blocks = static_cast<uint32_t>(num_blocks);
-    const int32_t grid_parts = p.partition_size ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
+    const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
     return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, flags, stream);
 }
 
@@ -471,11 +639,11 @@ extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const v
     if (lmax <= 0) return fail(PKV_EINVAL, "%s: lmax must be positive", fn);
     // tile rows of the contiguous slab: 16 (any multiple of rows-per-load works)
     constexpr int32_t kTile = 16;
-    if (partition_size % kTile) return fail(PKV_EINVAL, "%s: partition_size must be a multiple of 16", fn);
+    if (partition_size > 0 && partition_size % kTile) return fail(PKV_EINVAL, "%s: partition_size must be a multiple of 16", fn);
     const int32_t cap = std::min(max_context_len, lmax);
     AttnParams p = make_params(out, q, k, v, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
-                               partition_size, max_context_len, cap, workspace);
+                               partition_size, max_context_len, cap, workspace, workspace_bytes, head_dim);
     p.lmax = lmax;
-    const int32_t grid_parts = p.partition_size ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
+    const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
     return dispatch<false>(p, dtype, head_dim, kTile, num_seqs, grid_parts, flags, stream);
 }

@@ -84,12 +84,19 @@ __device__ inline unsigned word(const u32x4 &r, int w) {
     return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
 }
 
-// Grid = (num_kv_heads, parts, num_seqs), block = 64 * W. head_dim 128, 16-bit types.
-// U tiles per stage; stages are double-buffered in registers. At most 256 registers per lane
-// (two waves per SIMD), so two workgroups share a CU and one's start-up hides behind the other.
+template <int W>
+struct GqaLds {
+    float m[W][kMaxGroup], l[W][kMaxGroup];
+    float acc[W][kMaxGroup][128];
+};
+
+// Tokens [t0, t1) of sequence s for kv head kvh and its G query heads (t0 a multiple of 16,
+// t0 < t1 <= the length): the workgroup's merged result goes to sink. Uniform over the
+// workgroup; ends with a barrier, so the caller may run it again on the same LDS. head_dim 128,
+// 16-bit types; U tiles per stage, stages double-buffered in registers.
 template <class E, int B, bool PAGED, int W, int U>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
-    const AttnParams p) {
+__device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
+                                 GqaLds<W> &lds) {
     using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;          // tile rows
@@ -98,15 +105,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     static_assert(B % TR == 0, "block_size must be a multiple of 16");
     static_assert(64 % U == 0, "a stage must not straddle a table chunk");
 
-    __shared__ float s_m[W][kMaxGroup], s_l[W][kMaxGroup];
-    __shared__ float s_acc[W][kMaxGroup][D];
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
-    const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
     const int G = p.group;
     const int n = lane & 15, g = lane >> 4;
-    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
     const int jt0 = t0 / TR;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
 
@@ -125,14 +127,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             qv[kk] = n < G ? *reinterpret_cast<const u32x4 *>(qp + kk * 64) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
-    if (t0 >= t1) {
-        if (p.partition_size == 0)
-            for (int i = threadIdx.x; i < G * D; i += W * 64) E::store(p.out, row_q0 * D + i, 0.f);
-        return;
     }
 
     const char *kc = static_cast<const char *>(p.k);
@@ -289,10 +283,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s_acc[wave][n][8 * (4 * g + i) + j] = acc[j][i];
+            for (int j = 0; j < 8; ++j) lds.acc[wave][n][8 * (4 * g + i) + j] = acc[j][i];
         if (g == 0) {
-            s_m[wave][n] = m;
-            s_l[wave][n] = lsum;
+            lds.m[wave][n] = m;
+            lds.l[wave][n] = lsum;
         }
     }
     __syncthreads();
@@ -300,34 +294,90 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         const int h = idx / D, dd = idx % D;
         float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, lds.m[w][h]);
         const float Mr = Mx == -INFINITY ? 0.f : Mx;
         float L = 0.f, O = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float f = fast_exp2(s_m[w][h] - Mr);
-            L = fmaf(s_l[w][h], f, L);
-            O = fmaf(s_acc[w][h][dd], f, O);
+            const float f = fast_exp2(lds.m[w][h] - Mr);
+            L = fmaf(lds.l[w][h], f, L);
+            O = fmaf(lds.acc[w][h][dd], f, O);
         }
-        const int64_t row_q = row_q0 + h;
-        if (p.partition_size > 0) {
-            const int64_t wr = row_q * p.num_parts + part;
-            p.ws[wr * D + dd] = O;
+        if (sink.acc) {
+            sink.acc[h * sink.acc_stride + dd] = O;
             if (dd == 0) {
-                p.ws[p.ws_rows * D + wr] = Mx;
-                p.ws[p.ws_rows * (D + 1) + wr] = L;
+                sink.m[h * sink.ml_stride] = Mx;
+                sink.l[h * sink.ml_stride] = L;
             }
         } else {
-            E::store(p.out, row_q * D + dd, L > 0.f ? O / L : 0.f);
+            E::store(p.out, (row_q0 + h) * D + dd, L > 0.f ? O / L : 0.f);
         }
     }
+    __syncthreads();
+}
+
+// Per-item schedule: grid = (num_kv_heads, parts, num_seqs), block = 64 * W, the kv head fastest
+// so that a kv head's workgroups share XCDs (and the L2 holding a shared prefix). At most 256
+// registers per lane (two waves per SIMD): two workgroups share a CU and one's start-up hides
+// behind the other.
+template <class E, int B, bool PAGED, int W, int U>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
+    const AttnParams p) {
+    __shared__ GqaLds<W> lds;
+    const int kvh = blockIdx.x, part = blockIdx.y, s = blockIdx.z;
+    const int G = p.group;
+    const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
+    const int t1 = p.partition_size > 0 ? min(ctx, t0 + p.partition_size) : ctx;
+    if (t0 >= t1) {
+        if (p.partition_size == 0)
+            for (int i = threadIdx.x; i < G * 128; i += W * 64) E::store(p.out, row_q0 * 128 + i, 0.f);
+        return;
+    }
+    Sink sink{nullptr, nullptr, nullptr, 0, 0};
+    if (p.partition_size > 0) {
+        const int64_t wr = row_q0 * p.num_parts + part;  // head j: workspace row wr + j * num_parts
+        sink = Sink{p.ws + wr * 128, p.ws + p.ws_rows * 128 + wr, p.ws + p.ws_rows * 129 + wr,
+                    static_cast<int64_t>(p.num_parts) * 128, p.num_parts};
+    }
+    gqa_range<E, B, PAGED, W, U>(p, s, kvh, t0, t1, sink, lds);
+}
+
+// Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
+// (work rows = (sequence, kv head)); cut rows are merged by the balanced reduce pass.
+template <class E, int B, bool PAGED, int W, int U>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
+    const AttnParams p) {
+    __shared__ GqaLds<W> lds;
+    __shared__ uint32_t C[kBalancedMaxSeqs + 1];
+    __shared__ uint32_t part[W * 64];
+    balanced_prefix<W * 64>(p, C, part);
+    balanced_walk<128>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
+        const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+        gqa_range<E, B, PAGED, W, U>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
+    });
 }
 
 template <class E, int B, bool PAGED>
 int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>), dim3(p.num_kv_heads, grid_parts, num_seqs),
-                       dim3(kGqaWaves * 64), 0, stream, p);
-    return hip_status(hipGetLastError(), "grouped-query attention launch");
+    if (p.partition_size == PKV_PARTITION_BALANCED) {
+        AttnParams q = p;
+        q.tile_rows = 16;
+        q.rows_per_seq = p.num_kv_heads;
+        q.heads_per_row = p.group;
+        int rc = balanced_check(q);
+        if (rc) return rc;
+        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>), dim3(q.balanced_wgs),
+                           dim3(kGqaWaves * 64), 0, stream, q);
+        rc = hip_status(hipGetLastError(), "grouped-query attention launch");
+        return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
+    }
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>),
+                       dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
+    int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
+    if (rc || p.partition_size <= 0) return rc;
+    return launch_reduce(p, E::CODE, 128, num_seqs, stream);
 }
 
 template <class E, bool PAGED>
@@ -359,8 +409,7 @@ int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool
     else
         rc = paged ? launch_block<BF16, true>(p, block_size, num_seqs, grid_parts, stream)
                    : launch_block<BF16, false>(p, block_size, num_seqs, grid_parts, stream);
-    if (rc || p.partition_size == 0) return rc;
-    return launch_reduce(p, dtype, 128, num_seqs, stream);
+    return rc;
 }
 
 }  // namespace pkv

@@ -68,8 +68,11 @@ def _case(name):
     return _STATE[name]
 
 
+BALANCED = -1  # PKV_PARTITION_BALANCED
+
+
 def _modes(w):
-    ms = {0}
+    ms = {0, BALANCED}
     if w.partition_size:
         ms.add(w.partition_size)
     ms.add(max(w.block_size, 256))
@@ -121,7 +124,7 @@ def test_contiguous_companion(name):
     dt = TORCH_DTYPE[w.dtype]
     kd, vd, qd = to_device(k, dt, "cuda"), to_device(v, dt, "cuda"), to_device(w.q, dt, "cuda")
     cd = torch.from_numpy(ctx).cuda()
-    for P in (0, 256):
+    for P in (0, 256, BALANCED):
         out = torch.empty_like(qd)
         ws = kernels.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, int(ctx.max()), P)
         kernels.contiguous_attention_decode(out, qd, kd, vd, cd, int(ctx.max()), w.scale, P, ws)
@@ -143,6 +146,7 @@ def test_physical_permutation_is_bit_invariant(name):
     c = gpu_replay(w)
     base = gpu_attention(c, w, partition_size=0)
     base_split = gpu_attention(c, w, partition_size=256)
+    base_bal = gpu_attention(c, w, partition_size=BALANCED)
     N = w.num_blocks
     perm = torch.from_numpy(np.random.default_rng(11).permutation(N)).cuda()
     k2 = torch.empty_like(c.k)
@@ -152,7 +156,7 @@ def test_physical_permutation_is_bit_invariant(name):
     tb, ctx, mx = c.tables(w.batch)
     tb2 = torch.where(tb >= 0, perm[tb.clamp(min=0).long()].int(), tb)
     q = to_device(w.q, TORCH_DTYPE[w.dtype], "cuda")
-    for P, ref in ((0, base), (256, base_split)):
+    for P, ref in ((0, base), (256, base_split), (BALANCED, base_bal)):
         out = torch.empty_like(q)
         ws = kernels.alloc_workspace(q.shape[0], q.shape[1], q.shape[2], mx, P)
         kernels.paged_attention_decode(out, q, k2, v2, tb2, ctx, mx, w.scale, P, ws)
@@ -189,7 +193,7 @@ def test_edge_lengths(dtype, d):
     ref = oracle.attention_of(st, w)
     assert np.array_equal(ref[0], np.zeros_like(ref[0]))
     c = gpu_replay(w)
-    for P_ in (0, P, B):
+    for P_ in (0, P, B, BALANCED):
         for pad in (-1, 2**31 - 1):
             tb, ctx, mx = c.tables(w.batch, pad=pad)
             q = to_device(w.q, TORCH_DTYPE[dtype], "cuda")
@@ -208,12 +212,13 @@ def test_single_sequence_and_zero_lengths_batch():
     w = synth.decode_workload("one", 12, [777], 8, 8, 128, 16, "f16", 0.5, 0.5)
     st = oracle.replay(w)
     c = gpu_replay(w)
-    assert_close(gpu_attention(c, w, 0), oracle.attention_of(st, w), "f16", "S=1")
-    # every length zero: zeros, also in split mode
+    for P in (0, BALANCED):
+        assert_close(gpu_attention(c, w, P), oracle.attention_of(st, w), "f16", f"S=1 P={P}")
+    # every length zero: zeros, also in the split modes
     q = to_device(w.q, torch.float16, "cuda")
     tb, ctx, _ = c.tables(w.batch)
     zero = torch.zeros_like(ctx)
-    for P in (0, 64):
+    for P in (0, 64, BALANCED):
         out = torch.full_like(q, 7.0)
         ws = kernels.alloc_workspace(1, 8, 128, 1, P)
         kernels.paged_attention_decode(out, q, c.k, c.v, tb, zero, 1, w.scale, P, ws)
@@ -309,5 +314,5 @@ def test_long_context_spans_table_chunks(dtype, hq, hkv, B):
     st = oracle.replay(w)
     ref = oracle.attention_of(st, w)
     c = gpu_replay(w)
-    for P in (0, 1024):
+    for P in (0, 1024, BALANCED):
         assert_close(gpu_attention(c, w, partition_size=P), ref, dtype, f"long P={P}")
