@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and decode tokens/s, 13B shape"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PARTITION_BALANCED = -1  # the library's balanced split mode
 ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/attention.h",
                 "paged_kv_cache_416_amd/csrc/common.h"]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -75,7 +76,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="13b", choices=["13b", "sweep-b8", "sweep-b16", "sweep-b32", "gqa"])
-    ap.add_argument("--partition", type=int, default=-1, help="partition size; -1 = the workload's default")
+    ap.add_argument("--partition", default="default",
+                    help="partition size in tokens, 0 (single pass), 'balanced', or 'default' (the workload's)")
     ap.add_argument("--replicas", type=int, default=3, help="cache copies rotated across steps (defeats the MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contiguous", action="store_true")
@@ -151,7 +153,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w, default_P = make_workload(args.workload)
-    P = default_P if args.partition < 0 else args.partition
+    P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
+    if P is None:
+        P = int(args.partition)
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     S, hq, hkv, d, B, elt = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.elt_bytes
 
@@ -229,7 +233,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
-                     "kernel": "attn_decode_kernel" + ("+attn_reduce_kernel" if P else "")},
+                     "kernel": "attn_decode_kernel" + ("+attn_reduce_kernel" if P > 0 else "")
+                               + ("(balanced)+attn_reduce_balanced_kernel" if P == PARTITION_BALANCED else "")},
     }
 
     if args.copy_probe:

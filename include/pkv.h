@@ -56,6 +56,11 @@ typedef enum pkv_dtype {
 
 /* Attention flags. */
 #define PKV_FLAG_SCALAR_GQA 1u /* use the one-query-head-per-workgroup kernel even when G > 1 */
+/* The batch's sequences share blocks (a common prefix mapped by many block tables, slide 14:
+ * a system prompt shared like a library): load K/V through the caches, so that a block's
+ * re-reads by the other sequences hit the L2 / last-level cache. Without it K/V are streamed
+ * past the caches (non-temporal), which suits blocks read once per call. Paged cache only. */
+#define PKV_FLAG_CACHED_KV 2u
 
 /* partition_size value for the balanced split: the library cuts the whole batch's work into
  * equal shares, one per workgroup on the device (a (sequence, head) may be cut anywhere), and a
@@ -179,7 +184,7 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                 compute-unit count (results are still reproducible on one device).
  *  workspace:     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned;
  *                 may be NULL when partition_size == 0.
- *  flags:         PKV_FLAG_SCALAR_GQA or 0.
+ *  flags:         PKV_FLAG_SCALAR_GQA and/or PKV_FLAG_CACHED_KV, or 0; other bits are PKV_EINVAL.
  * Device-side guards (never faults on bad tables, but the result is then unspecified):
  * lengths are clamped to [0, min(max_context_len, max_blocks_per_seq*block_size)] and a
  * table entry outside [0, num_blocks) contributes no tokens.

@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_ENOMEM, PKV_ENOSEQ, PKV_EHIP, PKV_EUNSUPPORTED, PKV_EEXIST = 0, -1, -2, -3, -4, -5, -6
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_FLAG_SCALAR_GQA = 1
+PKV_FLAG_CACHED_KV = 2
 PKV_PARTITION_BALANCED = -1
 
 STATUS_NAMES = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_ENOMEM", -3: "PKV_ENOSEQ", -4: "PKV_EHIP",

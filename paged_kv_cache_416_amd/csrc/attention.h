@@ -234,13 +234,36 @@ __device__ inline u32x4 nt_load(const char *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// A buffer resource over the bytes [base, base + bytes) (raw, stride 0): a load whose offset
+// lies at or past the end returns zeros, so the hardware range check masks rows past a
+// sequence's end, and a zero-byte resource makes a tile read as zeros.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, uint32_t bytes) {
+    constexpr int kRawBufferConfig = 0x00020000;  // dword 3 of a gfx9 raw buffer descriptor
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, static_cast<int>(bytes), kRawBufferConfig);
+}
+
+// K/V loads. NT (the default): non-temporal, for blocks read once per call; otherwise through
+// the caches, for blocks several sequences of the batch read (a shared prefix), whose re-reads
+// then hit the L2 or the last-level cache instead of HBM.
+template <bool NT>
+__device__ inline u32x4 kv_load(const char *p) {
+    if constexpr (NT) return nt_load(p);
+    else return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <bool NT>
+__device__ inline u32x4 kv_buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    constexpr int kPolicy = NT ? 2 : 0;  // cache-policy bit nt
+    return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kPolicy);
+}
+
 // Compile-time shape of the tile walk for element type E, head_dim D, block_size B.
 
 // MFMA grouped-query kernel (attention_gqa.hip). gqa_mfma_supported tells whether a shape has
 // an MFMA build; launch_gqa_mfma enqueues it (and the reduce pass in split mode).
 bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
-int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int32_t num_seqs,
-                    int32_t grid_parts, hipStream_t stream);
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, bool cached,
+                    int32_t num_seqs, int32_t grid_parts, hipStream_t stream);
 // The partition merge (attention.hip), shared by both kernels.
 int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t num_seqs, hipStream_t stream);
 // The balanced schedule's merge of cut rows (attention.hip).

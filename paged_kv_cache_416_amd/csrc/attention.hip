@@ -68,7 +68,7 @@ struct MhaLds {
 // Tokens [t0, t1) of sequence s for query head h (t0 a multiple of the tile rows, t0 < t1 <= the
 // length): the workgroup's merged result goes to sink. Uniform over the workgroup; ends with a
 // barrier, so the caller may run it again on the same LDS.
-template <class E, int D, int B, bool PAGED, int W>
+template <class E, int D, int B, bool PAGED, int W, bool NT>
 __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int t1, const Sink &sink,
                                  MhaLds<W, D> &lds) {
     using SH = Shape<E, D, B>;
@@ -141,8 +141,8 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
             for (int l = 0; l < NL; ++l) {
                 const unsigned row = clamp ? min(l * RPI + r0, lim) : l * RPI + r0;
                 const unsigned off = row * (D * E::ELT) + c * (VEC * E::ELT);
-                S.k[u][l] = nt_load(kt + off);
-                S.v[u][l] = nt_load(vt + off);
+                S.k[u][l] = kv_load<NT>(kt + off);
+                S.v[u][l] = kv_load<NT>(vt + off);
             }
         }
     };
@@ -276,7 +276,7 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
 
 // Per-item schedule: grid = (parts, num_q_heads, num_seqs), block = 64 * W; one workgroup per
 // (sequence, query head[, partition]).
-template <class E, int D, int B, bool PAGED, int W>
+template <class E, int D, int B, bool PAGED, int W, bool NT>
 __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
     __shared__ MhaLds<W, D> lds;
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -294,12 +294,12 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         const int64_t wr = row_q * p.num_parts + part;
         sink = Sink{p.ws + wr * D, p.ws + p.ws_rows * D + wr, p.ws + p.ws_rows * (D + 1) + wr, 0, 0};
     }
-    mha_range<E, D, B, PAGED, W>(p, s, h, t0, t1, sink, lds);
+    mha_range<E, D, B, PAGED, W, NT>(p, s, h, t0, t1, sink, lds);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
 // (work rows = (sequence, query head)); cut rows are merged by attn_reduce_balanced_kernel.
-template <class E, int D, int B, bool PAGED, int W>
+template <class E, int D, int B, bool PAGED, int W, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_balanced_kernel(
     const AttnParams p) {
     __shared__ MhaLds<W, D> lds;
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_walk<D>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        mha_range<E, D, B, PAGED, W>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
+        mha_range<E, D, B, PAGED, W, NT>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
     });
 }
 
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnPar
 
 constexpr int kBalancedWaves = 4;
 
-template <class E, int D, int B, bool PAGED>
+template <class E, int D, int B, bool PAGED, bool NT>
 int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.partition_size == PKV_PARTITION_BALANCED) {
         AttnParams q = p;
@@ -406,12 +406,12 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
         q.heads_per_row = 1;
         int rc = balanced_check(q);
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves>), dim3(q.balanced_wgs),
+        hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves, NT>), dim3(q.balanced_wgs),
                            dim3(kBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, D, stream);
     }
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves>), dim3(grid_parts, p.num_q_heads, num_seqs),
+    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves, NT>), dim3(grid_parts, p.num_q_heads, num_seqs),
                        dim3(kThreads), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "attention launch");
     if (rc || p.partition_size <= 0) return rc;
@@ -419,29 +419,33 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
 }
 
 template <class E, int D, bool PAGED>
-int dispatch_block(const AttnParams &p, int32_t block_size, int32_t num_seqs, int32_t grid_parts,
+int dispatch_block(const AttnParams &p, int32_t block_size, bool cached, int32_t num_seqs, int32_t grid_parts,
                    hipStream_t stream) {
     if constexpr (!PAGED) {
-        return launch<E, D, 16, false>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+        return launch<E, D, 16, false, true>(p, num_seqs, grid_parts, stream);  // 16-row tiles
     } else {
+#define PKV_B(B) \
+    return cached ? launch<E, D, B, true, false>(p, num_seqs, grid_parts, stream) \
+                  : launch<E, D, B, true, true>(p, num_seqs, grid_parts, stream)
         switch (block_size) {
-        case 8: return launch<E, D, 8, true>(p, num_seqs, grid_parts, stream);
-        case 16: return launch<E, D, 16, true>(p, num_seqs, grid_parts, stream);
-        case 32: return launch<E, D, 32, true>(p, num_seqs, grid_parts, stream);
+        case 8: PKV_B(8);
+        case 16: PKV_B(16);
+        case 32: PKV_B(32);
         default: return fail(PKV_EUNSUPPORTED, "block_size %d not built (8, 16, 32)", block_size);
         }
+#undef PKV_B
     }
 }
 
 // One query head per workgroup (any G), then the merge pass of the split modes.
 template <bool PAGED>
-int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
-                      int32_t grid_parts, hipStream_t stream) {
+int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, bool cached,
+                      int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     int rc;
 #define PKV_HD(E)                                                                                 \
     switch (head_dim) {                                                                           \
-    case 64: rc = dispatch_block<E, 64, PAGED>(p, block_size, num_seqs, grid_parts, stream); break;   \
-    case 128: rc = dispatch_block<E, 128, PAGED>(p, block_size, num_seqs, grid_parts, stream); break; \
+    case 64: rc = dispatch_block<E, 64, PAGED>(p, block_size, cached, num_seqs, grid_parts, stream); break; \
+    case 128: rc = dispatch_block<E, 128, PAGED>(p, block_size, cached, num_seqs, grid_parts, stream); break; \
     default: return fail(PKV_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);          \
     }
     switch (dtype) {
@@ -457,9 +461,10 @@ int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int3
 template <bool PAGED>
 int dispatch(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
              int32_t grid_parts, uint32_t flags, hipStream_t stream) {
+    const bool cached = PAGED && (flags & PKV_FLAG_CACHED_KV);
     if (p.group > 1 && !(flags & PKV_FLAG_SCALAR_GQA) && gqa_mfma_supported(dtype, head_dim, block_size, p.group))
-        return launch_gqa_mfma(p, dtype, block_size, PAGED, num_seqs, grid_parts, stream);
-    return dispatch_per_head<PAGED>(p, dtype, head_dim, block_size, num_seqs, grid_parts, stream);
+        return launch_gqa_mfma(p, dtype, block_size, PAGED, cached, num_seqs, grid_parts, stream);
+    return dispatch_per_head<PAGED>(p, dtype, head_dim, block_size, cached, num_seqs, grid_parts, stream);
 }
 
 // Checks shared by the paged and contiguous entry points.
@@ -607,6 +612,7 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     int rc = check_common(fn, out, q, k_cache, v_cache, context_lens, max_context_len, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, scale, partition_size, workspace, workspace_bytes, dtype);
     if (rc || num_seqs == 0) return rc;
+    if (flags & ~(PKV_FLAG_SCALAR_GQA | PKV_FLAG_CACHED_KV)) return fail(PKV_EINVAL, "%s: unknown flags %#x", fn, flags);
     if (block_size != 8 && block_size != 16 && block_size != 32)
         return fail(PKV_EUNSUPPORTED, "%s: block_size %d not built (8, 16, 32)", fn, block_size);
     if (partition_size > 0 && partition_size % block_size)
@@ -636,6 +642,7 @@ extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const v
     int rc = check_common(fn, out, q, k, v, context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
                           head_dim, scale, partition_size, workspace, workspace_bytes, dtype);
     if (rc || num_seqs == 0) return rc;
+    if (flags & ~(PKV_FLAG_SCALAR_GQA | PKV_FLAG_CACHED_KV)) return fail(PKV_EINVAL, "%s: unknown flags %#x", fn, flags);
     if (lmax <= 0) return fail(PKV_EINVAL, "%s: lmax must be positive", fn);
     // tile rows of the contiguous slab: 16 (any multiple of rows-per-load works)
     constexpr int32_t kTile = 16;

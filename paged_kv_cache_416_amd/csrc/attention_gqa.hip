@@ -94,7 +94,7 @@ struct GqaLds {
 // t0 < t1 <= the length): the workgroup's merged result goes to sink. Uniform over the
 // workgroup; ends with a barrier, so the caller may run it again on the same LDS. head_dim 128,
 // 16-bit types; U tiles per stage, stages double-buffered in registers.
-template <class E, int B, bool PAGED, int W, int U>
+template <class E, int B, bool PAGED, int W, int U, bool NT>
 __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
                                  GqaLds<W> &lds) {
     using M = Mfma<E>;
@@ -154,27 +154,25 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         bool in[U];  // tile belongs to this wave (false: a stand-in, masked out)
     };
 
-    // Every load is unconditional (exact wait counts). With clamp set, a tile past the wave's
-    // last is replaced by its last tile and a row at or past t1 by the row before t1: in bounds
-    // and written; consume() masks them out.
+    // Every load is unconditional (exact wait counts) and goes through a buffer resource that
+    // ends at the tile's last row inside [t0, t1): rows past it, a tile past the wave's last
+    // (clamp) and a tile whose table entry is rejected read as zeros; consume() masks them out.
+    const unsigned koff = n * ROWB + g * 16;      // + kk * 64: row n, chunk 4*kk + g
+    const unsigned voff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n
     auto issue = [&](Stage &S, int kc0, int st, bool clamp) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int k = kc0 + st * U + u;
+            const int k = kc0 + st * U + u;
             S.in[u] = k < nk;
-            if (clamp) k = min(k, nk - 1);
-            const int64_t tile = tile_offset(k, kc0, S.ok[u]);
-            const char *kt = kc + tile, *vt = vc + tile;
+            const int kr = clamp ? min(k, nk - 1) : k;  // table lane to read
+            const int64_t tile = tile_offset(kr, kc0, S.ok[u]);
             S.tok0[u] = (jt0 + wave + k * W) * TR;
-            const int lim = t1 - 1 - S.tok0[u];
-            const unsigned krow = clamp ? min(n, lim) : n;
+            const int rows = S.in[u] && S.ok[u] ? min(TR, t1 - S.tok0[u]) : 0;
+            const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) S.k[u][kk] = nt_load(kt + (krow * ROWB + (4 * kk + g) * 16));
+            for (int kk = 0; kk < 4; ++kk) S.k[u][kk] = kv_buffer_load<NT>(kr_, koff + kk * 64);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const unsigned vrow = clamp ? min(4 * g + i, lim) : 4 * g + i;
-                S.v[u][i] = nt_load(vt + (vrow * ROWB + n * 16));
-            }
+            for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<NT>(vr_, voff + i * ROWB);
         }
     };
 
@@ -221,9 +219,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
             }
             const u32x2 pt = {static_cast<unsigned>(pb[0]) | (static_cast<unsigned>(pb[1]) << 16),
                               static_cast<unsigned>(pb[2]) | (static_cast<unsigned>(pb[3]) << 16)};
-            // a rejected table entry's tile was read from a clamped block (its values may not be
-            // finite) and a stand-in tile adds nothing: neither enters the weighted sum
-            if (!S.ok[u] || (tail && !S.in[u])) continue;
+            // (a rejected or stand-in tile reads as zeros and its weights are zero)
             // V^T operand of MFMA j: element j of the lane's 4 V rows
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -320,7 +316,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 // so that a kv head's workgroups share XCDs (and the L2 holding a shared prefix). At most 256
 // registers per lane (two waves per SIMD): two workgroups share a CU and one's start-up hides
 // behind the other.
-template <class E, int B, bool PAGED, int W, int U>
+template <class E, int B, bool PAGED, int W, int U, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -341,12 +337,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         sink = Sink{p.ws + wr * 128, p.ws + p.ws_rows * 128 + wr, p.ws + p.ws_rows * 129 + wr,
                     static_cast<int64_t>(p.num_parts) * 128, p.num_parts};
     }
-    gqa_range<E, B, PAGED, W, U>(p, s, kvh, t0, t1, sink, lds);
+    gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, t0, t1, sink, lds);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
 // (work rows = (sequence, kv head)); cut rows are merged by the balanced reduce pass.
-template <class E, int B, bool PAGED, int W, int U>
+template <class E, int B, bool PAGED, int W, int U, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -355,11 +351,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_prefix<W * 64>(p, C, part);
     balanced_walk<128>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        gqa_range<E, B, PAGED, W, U>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
+        gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
 }
 
-template <class E, int B, bool PAGED>
+template <class E, int B, bool PAGED, bool NT>
 int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.partition_size == PKV_PARTITION_BALANCED) {
         AttnParams q = p;
@@ -368,12 +364,12 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
         q.heads_per_row = p.group;
         int rc = balanced_check(q);
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>), dim3(q.balanced_wgs),
+        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, NT>), dim3(q.balanced_wgs),
                            dim3(kGqaWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "grouped-query attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
     }
-    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles>),
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, NT>),
                        dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
     if (rc || p.partition_size <= 0) return rc;
@@ -381,12 +377,16 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
 }
 
 template <class E, bool PAGED>
-int launch_block(const AttnParams &p, int32_t block_size, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
+int launch_block(const AttnParams &p, int32_t block_size, bool cached, int32_t num_seqs, int32_t grid_parts,
+                 hipStream_t stream) {
     if constexpr (!PAGED) {
-        return launch_one<E, 16, false>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+        return launch_one<E, 16, false, true>(p, num_seqs, grid_parts, stream);  // 16-row tiles
     } else {
-        return block_size == 32 ? launch_one<E, 32, true>(p, num_seqs, grid_parts, stream)
-                                : launch_one<E, 16, true>(p, num_seqs, grid_parts, stream);
+        if (block_size == 32)
+            return cached ? launch_one<E, 32, true, false>(p, num_seqs, grid_parts, stream)
+                          : launch_one<E, 32, true, true>(p, num_seqs, grid_parts, stream);
+        return cached ? launch_one<E, 16, true, false>(p, num_seqs, grid_parts, stream)
+                      : launch_one<E, 16, true, true>(p, num_seqs, grid_parts, stream);
     }
 }
 
@@ -397,19 +397,16 @@ bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int
            group >= 2 && group <= kMaxGroup;
 }
 
-int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int32_t num_seqs,
-                    int32_t grid_parts, hipStream_t stream) {
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, bool cached,
+                    int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.num_kv_heads > 65535 || grid_parts > 65535)
         return fail(PKV_EINVAL, "grouped-query attention: %d kv heads x %d partitions exceed the grid", p.num_kv_heads,
                     grid_parts);
-    int rc;
     if (dtype == PKV_F16)
-        rc = paged ? launch_block<F16, true>(p, block_size, num_seqs, grid_parts, stream)
-                   : launch_block<F16, false>(p, block_size, num_seqs, grid_parts, stream);
-    else
-        rc = paged ? launch_block<BF16, true>(p, block_size, num_seqs, grid_parts, stream)
-                   : launch_block<BF16, false>(p, block_size, num_seqs, grid_parts, stream);
-    return rc;
+        return paged ? launch_block<F16, true>(p, block_size, cached, num_seqs, grid_parts, stream)
+                     : launch_block<F16, false>(p, block_size, cached, num_seqs, grid_parts, stream);
+    return paged ? launch_block<BF16, true>(p, block_size, cached, num_seqs, grid_parts, stream)
+                 : launch_block<BF16, false>(p, block_size, cached, num_seqs, grid_parts, stream);
 }
 
 }  // namespace pkv

@@ -74,6 +74,7 @@ def _attn(**kw):
     (dict(S=70000), _lib.PKV_EINVAL),
     (dict(P=24), _lib.PKV_EINVAL),            # not a multiple of block_size
     (dict(P=-2), _lib.PKV_EINVAL),            # negative, and not the balanced mode
+    (dict(flags=8), _lib.PKV_EINVAL),         # unknown flag bit
     (dict(P=32), _lib.PKV_EINVAL),            # split mode without workspace
     (dict(P=32, ws=FAKE, ws_bytes=100), _lib.PKV_EINVAL),  # workspace too small
     (dict(scale=float("nan")), _lib.PKV_EINVAL),

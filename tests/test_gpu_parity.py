@@ -69,6 +69,7 @@ def _case(name):
 
 
 BALANCED = -1  # PKV_PARTITION_BALANCED
+CACHED_KV = 2  # PKV_FLAG_CACHED_KV
 
 
 def _modes(w):
@@ -98,6 +99,8 @@ def test_attention_matches_oracle(name):
         out = gpu_attention(c, w, partition_size=P)
         err = assert_close(out, ref, w.dtype, f"{name} P={P}")
         say(f"  [{name}] P={P} max abs err {err:.3e}")
+        # loading through the caches changes no arithmetic: bit-identical
+        assert bits_equal(gpu_attention(c, w, partition_size=P, flags=CACHED_KV), out)
         if w.num_q_heads > w.num_kv_heads:
             out2 = gpu_attention(c, w, partition_size=P, flags=1)
             assert_close(out2, ref, w.dtype, f"{name} P={P} scalar-gqa")
