@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and decode tokens/s, 13B shape"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 PARTITION_BALANCED = -1  # the library's balanced split mode
+FLAG_CACHED_KV = 2  # the library's cached K/V load flag
 ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/attention.h",
                 "paged_kv_cache_416_amd/csrc/common.h"]
 PROFILES = os.path.join(ROOT, "profiles")
@@ -82,7 +83,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain elementwise kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "CMD"))
@@ -91,13 +92,16 @@ def parse():
 
 
 def make_workload(name):
+    """(workload, default partition size, default flags)."""
     import synth
     if name == "13b":
-        return synth.llama13b(), 0
+        return synth.llama13b(), 0, 0
     if name.startswith("sweep-b"):
-        return synth.block_sweep(block_size=int(name[7:])), 0
+        return synth.block_sweep(block_size=int(name[7:])), 0, 0
     if name == "gqa":
-        return synth.gqa_shared_prefix(), 512
+        # every sequence maps the same 1024-token prefix blocks: the scheduler, which built the
+        # tables from reference counts, asks for cached K/V loads
+        return synth.gqa_shared_prefix(), 512, FLAG_CACHED_KV
     raise ValueError(name)
 
 
@@ -152,7 +156,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w, default_P = make_workload(args.workload)
+    w, default_P, default_flags = make_workload(args.workload)
+    flags = default_flags if args.flags < 0 else args.flags
     P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
     if P is None:
         P = int(args.partition)
@@ -186,7 +191,7 @@ def main():
 
     def attend(i):
         r = i % args.replicas
-        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, args.flags)
+        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, flags)
 
     def one_step(i):
         r = i % args.replicas
@@ -208,7 +213,7 @@ def main():
 
     value = (unique_b + w_bytes) / (ms_per_step * 1e-3) / 1e9
     achieved = unique_b / (attn_us * 1e-6) / 1e9
-    traffic = read_counters(w.name) if P == 0 and args.flags == 0 else None
+    traffic = read_counters(w.name) if P == 0 and flags == 0 else None
 
     result = {
         "metric": METRIC,
@@ -225,7 +230,7 @@ def main():
         "data": "synthetic (seeded N(0,1)*0.5 keys/values, seeded context lengths and physical block order)",
         "config": {"workload": w.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": B, "sum_context": int(ctx.sum()), "max_context": int(ctx.max()),
-                   "partition_size": P, "replicas": args.replicas},
+                   "partition_size": P, "flags": flags, "replicas": args.replicas},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "attention_us": round(attn_us, 2),
@@ -249,7 +254,7 @@ def main():
         del src, dst
 
     if not args.no_contiguous:
-        result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_us)
+        result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_us, flags)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, P, unique_b, args.cpu_seconds)
@@ -257,7 +262,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def contiguous_leg(w, P, args, dev, dt, paged_us):
+def contiguous_leg(w, P, args, dev, dt, paged_us, flags):
     """The same attention on a contiguous [S, Hkv, Lmax, D] cache: the indirection's price."""
     import numpy as np
     import torch
@@ -288,7 +293,7 @@ def contiguous_leg(w, P, args, dev, dt, paged_us):
 
     def attend(i):
         r = i % args.replicas
-        kernels.contiguous_attention_decode(out, q, kd[r], vd[r], cd, lmax, w.scale, P, ws, args.flags)
+        kernels.contiguous_attention_decode(out, q, kd[r], vd[r], cd, lmax, w.scale, P, ws, flags & ~FLAG_CACHED_KV)
 
     for i in range(10):
         attend(i)

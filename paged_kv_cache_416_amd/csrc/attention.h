@@ -108,6 +108,7 @@ struct AttnParams {
     int32_t tile_rows;       // balanced schedule: rows (tokens) per tile
     int32_t rows_per_seq;    // balanced schedule: work rows per sequence (query heads, or kv heads)
     int32_t heads_per_row;   // balanced schedule: query heads one work row serves
+    int32_t head_major;      // balanced schedule: rows ordered head-major (1) or sequence-major (0)
 };
 
 // Where a workgroup's merged result for one work row goes: acc == nullptr means the final,
@@ -126,18 +127,26 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
 // ---------------------------------------------------------------- balanced schedule
-// The work rows of the batch, sequence by sequence, each cut into tiles of tile_rows tokens,
-// form one list of T tiles; workgroup g takes tiles [b(g), b(g+1)), b(g) = floor(g*T/W). A row
-// that one workgroup holds whole is written to the output; a row cut between workgroups leaves
-// one partial result per workgroup in the workspace (slot 2g for the workgroup's first row,
-// 2g+1 for its last), merged in workgroup order by attn_reduce_balanced_kernel.
+// The work rows of the batch, each cut into tiles of tile_rows tokens, form one list of T tiles,
+// sequence-major (row = s * rows_per_seq + h) or head-major (row = h * num_seqs + s). Workgroup
+// g takes the share v = virtual(g) of it, tiles [b(v), b(v+1)), b(v) = floor(v*T/W). Workgroups
+// are dealt to the 8 XCDs round-robin, so virtual() gives each XCD a contiguous run of shares:
+// with head-major rows an XCD then serves few kv heads, and a block that many sequences share
+// stays in that XCD's L2. A row one workgroup holds whole is written to the output; a row cut
+// between workgroups leaves one partial result per share in the workspace (slot 2v for the
+// share's first row, 2v+1 for its last), merged in share order by attn_reduce_balanced_kernel.
 constexpr int kBalancedMaxSeqs = 4096;
 constexpr int kBalancedWgsPerCu = 2;
+constexpr int kXcds = 8;
 
-__device__ inline int64_t balanced_begin(int64_t g, int64_t T, int64_t nwg) { return g * T / nwg; }
+__device__ inline int64_t balanced_begin(int64_t v, int64_t T, int64_t nwg) { return v * T / nwg; }
 
-// The workgroup whose range holds tile x (0 <= x < T).
+// The share holding tile x (0 <= x < T).
 __device__ inline int64_t balanced_owner(int64_t x, int64_t T, int64_t nwg) { return ((x + 1) * nwg - 1) / T; }
+
+__device__ inline int64_t balanced_virtual(int64_t g, int64_t nwg) {
+    return nwg % kXcds == 0 ? (g % kXcds) * (nwg / kXcds) + g / kXcds : g;
+}
 
 // C[s] = tiles per row of the sequences before s, for s = 0 .. S (LDS, all threads of the
 // block); lengths clamped as everywhere else. Ends with a barrier.
@@ -166,43 +175,61 @@ __device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_
     __syncthreads();
 }
 
-// Walk this workgroup's share of the balanced list: body(s, row, tile_begin, tile_end, sink)
-// for each row segment, in order. Uniform over the workgroup.
-template <int D, class Body>
-__device__ inline void balanced_walk(const AttnParams &p, const uint32_t *C, Body &&body) {
-    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, g = blockIdx.x;
-    const int64_t T = R * C[p.num_seqs];
-    if (T == 0) return;
-    int64_t pos = balanced_begin(g, T, nwg);
-    const int64_t end = balanced_begin(g + 1, T, nwg);
-    if (pos >= end) return;
-    int lo = 0, hi = p.num_seqs;  // largest s with R*C[s] <= pos (it has tiles: R*C[s+1] > pos)
+// Row of list position x (0 <= x < T): its sequence s, head h and first tile's position row0.
+template <bool HEAD_MAJOR>
+__device__ inline void balanced_locate(const uint32_t *C, int S, int64_t R, int64_t x, int &s, int &h,
+                                       int64_t &row0) {
+    const int64_t Ctot = C[S];
+    int64_t rem = x;
+    if constexpr (HEAD_MAJOR) {
+        h = static_cast<int>(x / Ctot);
+        rem = x - h * Ctot;
+    }
+    const int64_t scale = HEAD_MAJOR ? 1 : R;
+    int lo = 0, hi = S;  // largest s with scale*C[s] <= rem: it has tiles (scale*C[s+1] > rem)
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (R * C[mid] <= pos) lo = mid; else hi = mid;
+        if (scale * C[mid] <= rem) lo = mid; else hi = mid;
     }
-    int s = lo;
-    bool first = true;
+    s = lo;
+    if constexpr (HEAD_MAJOR) {
+        row0 = h * Ctot + C[s];
+    } else {
+        const int64_t n = C[s + 1] - C[s];
+        h = static_cast<int>((x - R * C[s]) / n);
+        row0 = R * C[s] + h * n;
+    }
+}
+
+// Walk this workgroup's share: body(s, h, tile_begin, tile_end, sink) per row segment, in order.
+// Uniform over the workgroup.
+template <int D, bool HEAD_MAJOR, class Body>
+__device__ inline void balanced_walk(const AttnParams &p, const uint32_t *C, Body &&body) {
+    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs;
+    const int64_t T = R * C[p.num_seqs];
+    if (T == 0) return;
+    const int64_t v = balanced_virtual(blockIdx.x, nwg);
+    int64_t pos = balanced_begin(v, T, nwg);
+    const int64_t end = balanced_begin(v + 1, T, nwg);
     const int64_t slot_floats = static_cast<int64_t>(p.heads_per_row) * (D + 2);
+    bool first = true;
     while (pos < end) {
-        const int64_t n = C[s + 1] - C[s], base = R * C[s];
-        const int row = static_cast<int>((pos - base) / n);
-        const int64_t row0 = base + row * n;
+        int s, h;
+        int64_t row0;
+        balanced_locate<HEAD_MAJOR>(C, p.num_seqs, R, pos, s, h, row0);
+        const int64_t n = C[s + 1] - C[s];
         const int ta = static_cast<int>(pos - row0);
         const int tb = static_cast<int>(end - row0 < n ? end - row0 : n);
         Sink sink{nullptr, nullptr, nullptr, 0, 0};
         if (ta != 0 || tb != n) {
-            float *slot = p.ws + (2 * g + (first ? 0 : 1)) * slot_floats;
+            float *slot = p.ws + (2 * v + (first ? 0 : 1)) * slot_floats;
             sink = Sink{slot, slot + p.heads_per_row * D, slot + p.heads_per_row * (D + 1), D, 1};
         }
-        body(s, row, ta, tb, sink);
+        body(s, h, ta, tb, sink);
         first = false;
         pos = row0 + tb;
-        if (pos == base + R * n)  // past the sequence's last row: next sequence with tiles
-            do ++s; while (s < p.num_seqs && C[s + 1] == C[s]);
     }
 }
-
 
 // DPP lane moves within a row of 16 lanes.
 constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]

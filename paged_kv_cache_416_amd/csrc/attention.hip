@@ -306,7 +306,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
     balanced_prefix<W * 64>(p, C, part);
-    balanced_walk<D>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
+    balanced_walk<D, false>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
         mha_range<E, D, B, PAGED, W, NT>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnPar
         }
         __syncthreads();
     }
-    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, T = R * red[1][0];
+    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, Ctot = red[1][0], T = R * Ctot;
     const int64_t n = (clamp_ctx(p.ctx_lens[s], p.ctx_cap) + TR - 1) / TR;
     const int H = p.heads_per_row;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(row) * H;
@@ -366,11 +366,12 @@ __global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnPar
         for (int i = t; i < H * D; i += 256) E::store(p.out, row_q0 * D + i, 0.f);
         return;
     }
-    const int64_t row0 = R * red[0][0] + row * n;
+    const int64_t row0 = p.head_major ? row * Ctot + red[0][0] : R * red[0][0] + row * n;
+    // shares, in share order (the workgroup that ran share v is the one with virtual index v)
     const int64_t g0 = balanced_owner(row0, T, nwg), g1 = balanced_owner(row0 + n - 1, T, nwg);
     if (g0 == g1) return;
     const int64_t slot_floats = static_cast<int64_t>(H) * (D + 2);
-    // the first owner's part of this row is its first row only if its range starts on the row
+    // the first share's part of this row is its first row only if the share starts on the row
     const int64_t first_slot = balanced_begin(g0, T, nwg) < row0 ? 2 * g0 + 1 : 2 * g0;
     // workgroups with an empty range (more workgroups than tiles) hold nothing and are skipped
     auto empty = [&](int64_t g) { return balanced_begin(g + 1, T, nwg) == balanced_begin(g, T, nwg); };
@@ -404,6 +405,7 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
         q.tile_rows = Shape<E, D, B>::TR;
         q.rows_per_seq = p.num_q_heads;
         q.heads_per_row = 1;
+        q.head_major = 0;
         int rc = balanced_check(q);
         if (rc) return rc;
         hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves, NT>), dim3(q.balanced_wgs),

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
-// (work rows = (sequence, kv head)); cut rows are merged by the balanced reduce pass.
+// (work rows = (kv head, sequence), head-major); cut rows are merged by the balanced reduce pass.
 template <class E, int B, bool PAGED, int W, int U, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
     const AttnParams p) {
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
     balanced_prefix<W * 64>(p, C, part);
-    balanced_walk<128>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
+    balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
         gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
@@ -362,6 +362,7 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
         q.tile_rows = 16;
         q.rows_per_seq = p.num_kv_heads;
         q.heads_per_row = p.group;
+        q.head_major = 1;  // an XCD's shares cover few kv heads: shared blocks stay in its L2
         int rc = balanced_check(q);
         if (rc) return rc;
         hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, NT>), dim3(q.balanced_wgs),
