@@ -160,8 +160,8 @@ int pkv_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_la
 
 /* Bytes of fp32 workspace a split mode needs:
  *  partition_size > 0: num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4;
- *  PKV_PARTITION_BALANCED: 2 * (2 * the current device's compute units) * num_q_heads * (head_dim + 2) * 4
- *                          (0 if the device cannot be queried);
+ *  PKV_PARTITION_BALANCED: W * (2 * num_q_heads * (head_dim + 2) * 4 + 8) + 4097 * 4, where W is
+ *                          2 * the current device's compute units (0 if the device cannot be queried);
  *  partition_size == 0: 0. */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_size);

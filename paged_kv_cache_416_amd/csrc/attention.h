@@ -148,8 +148,21 @@ __device__ inline int64_t balanced_virtual(int64_t g, int64_t nwg) {
     return nwg % kXcds == 0 ? (g % kXcds) * (nwg / kXcds) + g / kXcds : g;
 }
 
+// Where the prefix sums C live in the workspace: after the 2 * balanced_wgs result slots.
+__device__ inline uint32_t *balanced_prefix_out(const AttnParams &p) {
+    return reinterpret_cast<uint32_t *>(p.ws + 2 * static_cast<int64_t>(p.balanced_wgs) * p.heads_per_row *
+                                                   (p.head_dim + 2));
+}
+
+// One record per share, after C: the (sequence, head) of the cut row whose last tile the share
+// holds (the merge pass merges that row), or -1.
+__device__ inline int32_t *balanced_records(const AttnParams &p) {
+    return reinterpret_cast<int32_t *>(balanced_prefix_out(p) + kBalancedMaxSeqs + 1);
+}
+
 // C[s] = tiles per row of the sequences before s, for s = 0 .. S (LDS, all threads of the
-// block); lengths clamped as everywhere else. Ends with a barrier.
+// block); lengths clamped as everywhere else. Ends with a barrier (except workgroup 0's copy
+// of C into the workspace, which the merge pass reads after this kernel).
 template <int NT>
 __device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_t *part) {
     const int t = threadIdx.x, S = p.num_seqs, TR = p.tile_rows;
@@ -173,6 +186,20 @@ __device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_
         }
     if (t == NT - 1) C[S] = part[NT - 1];
     __syncthreads();
+    // workgroup 0 leaves C in the workspace, after the slots, for the merge pass
+    if (blockIdx.x == 0) {
+        uint32_t *out = balanced_prefix_out(p);
+        for (int i = t; i <= S; i += NT) out[i] = C[i];
+    }
+}
+
+// Outputs of sequences with no tokens are zeros; the workgroups share them out.
+template <class E, int D, int NT>
+__device__ inline void balanced_zero_empty(const AttnParams &p, const uint32_t *C) {
+    for (int s = blockIdx.x; s < p.num_seqs; s += gridDim.x)
+        if (C[s + 1] == C[s])
+            for (int i = threadIdx.x; i < p.num_q_heads * D; i += NT)
+                E::store(p.out, static_cast<int64_t>(s) * p.num_q_heads * D + i, 0.f);
 }
 
 // Row of list position x (0 <= x < T): its sequence s, head h and first tile's position row0.
@@ -207,8 +234,10 @@ template <int D, bool HEAD_MAJOR, class Body>
 __device__ inline void balanced_walk(const AttnParams &p, const uint32_t *C, Body &&body) {
     const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs;
     const int64_t T = R * C[p.num_seqs];
-    if (T == 0) return;
     const int64_t v = balanced_virtual(blockIdx.x, nwg);
+    int32_t *rec = balanced_records(p) + 2 * v;
+    if (threadIdx.x == 0) rec[0] = rec[1] = -1;
+    if (T == 0) return;
     int64_t pos = balanced_begin(v, T, nwg);
     const int64_t end = balanced_begin(v + 1, T, nwg);
     const int64_t slot_floats = static_cast<int64_t>(p.heads_per_row) * (D + 2);
@@ -224,6 +253,10 @@ __device__ inline void balanced_walk(const AttnParams &p, const uint32_t *C, Bod
         if (ta != 0 || tb != n) {
             float *slot = p.ws + (2 * v + (first ? 0 : 1)) * slot_floats;
             sink = Sink{slot, slot + p.heads_per_row * D, slot + p.heads_per_row * (D + 1), D, 1};
+        }
+        if (first && ta != 0 && tb == n && threadIdx.x == 0) {  // this share ends a cut row: merge it
+            rec[0] = s;
+            rec[1] = h;
         }
         body(s, h, ta, tb, sink);
         first = false;

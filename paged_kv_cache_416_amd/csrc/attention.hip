@@ -306,6 +306,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
     balanced_prefix<W * 64>(p, C, part);
+    balanced_zero_empty<E, D, W * 64>(p, C);
     balanced_walk<D, false>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
@@ -335,62 +336,42 @@ __global__ __launch_bounds__(D) void attn_reduce_kernel(const AttnParams p) {
     E::store(p.out, row_q * D + i, L > 0.f ? O / L : 0.f);
 }
 
-// The balanced schedule's merge: grid = (rows_per_seq, num_seqs), block = 256. A row with no
-// tiles gets zeros; a row one workgroup held whole was written by it; a cut row's partial results
-// (one per workgroup that held part of it) are merged here in workgroup order.
+// The balanced schedule's merge: grid = balanced_wgs, block = 256. Share v merges the cut row
+// whose last tile it holds (if any), from the partial results of the shares that hold parts of
+// it, in share order. Rows held whole by one share were written by it; rows of sequences with
+// no tokens were zeroed by the attention kernel.
 template <class E, int D>
 __global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnParams p) {
-    __shared__ uint32_t red[2][256];
-    const int row = blockIdx.x, s = blockIdx.y, t = threadIdx.x, TR = p.tile_rows;
-    uint32_t before = 0, all = 0;
-    for (int i = t; i < p.num_seqs; i += 256) {
-        const uint32_t n = (clamp_ctx(p.ctx_lens[i], p.ctx_cap) + TR - 1) / TR;
-        all += n;
-        if (i < s) before += n;
-    }
-    red[0][t] = before;
-    red[1][t] = all;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if (t < o) {
-            red[0][t] += red[0][t + o];
-            red[1][t] += red[1][t + o];
-        }
-        __syncthreads();
-    }
-    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, Ctot = red[1][0], T = R * Ctot;
-    const int64_t n = (clamp_ctx(p.ctx_lens[s], p.ctx_cap) + TR - 1) / TR;
+    const int64_t v = blockIdx.x;
+    const int32_t *rec = balanced_records(p) + 2 * v;
+    const int s = rec[0], row = rec[1];
+    if (s < 0) return;
+    const uint32_t *C = balanced_prefix_out(p);  // written by the attention kernel's workgroup 0
+    const int64_t R = p.rows_per_seq, nwg = p.balanced_wgs, Ctot = C[p.num_seqs], T = R * Ctot;
+    const int64_t n = C[s + 1] - C[s];
     const int H = p.heads_per_row;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(row) * H;
-    if (n == 0) {
-        for (int i = t; i < H * D; i += 256) E::store(p.out, row_q0 * D + i, 0.f);
-        return;
-    }
-    const int64_t row0 = p.head_major ? row * Ctot + red[0][0] : R * red[0][0] + row * n;
-    // shares, in share order (the workgroup that ran share v is the one with virtual index v)
-    const int64_t g0 = balanced_owner(row0, T, nwg), g1 = balanced_owner(row0 + n - 1, T, nwg);
-    if (g0 == g1) return;
+    const int64_t row0 = p.head_major ? row * Ctot + C[s] : R * C[s] + row * n;
+    const int64_t g0 = balanced_owner(row0, T, nwg), g1 = v;
     const int64_t slot_floats = static_cast<int64_t>(H) * (D + 2);
     // the first share's part of this row is its first row only if the share starts on the row
     const int64_t first_slot = balanced_begin(g0, T, nwg) < row0 ? 2 * g0 + 1 : 2 * g0;
-    // workgroups with an empty range (more workgroups than tiles) hold nothing and are skipped
+    // shares with an empty range (more shares than tiles) hold nothing and are skipped
     auto empty = [&](int64_t g) { return balanced_begin(g + 1, T, nwg) == balanced_begin(g, T, nwg); };
-    for (int i = t; i < H * D; i += 256) {
+    for (int i = threadIdx.x; i < H * D; i += 256) {
         const int j = i / D, d = i % D;
-        float M = -INFINITY;
+        // one pass over the shares with a running max (the shares' loads are independent)
+        float M = -INFINITY, L = 0.f, O = 0.f;
         for (int64_t g = g0; g <= g1; ++g) {
             if (empty(g)) continue;
             const float *slot = p.ws + (g == g0 ? first_slot : 2 * g) * slot_floats;
-            M = fmaxf(M, slot[H * D + j]);
-        }
-        const float Mr = M == -INFINITY ? 0.f : M;
-        float L = 0.f, O = 0.f;
-        for (int64_t g = g0; g <= g1; ++g) {
-            if (empty(g)) continue;
-            const float *slot = p.ws + (g == g0 ? first_slot : 2 * g) * slot_floats;
-            const float f = fast_exp2(slot[H * D + j] - Mr);
-            L = fmaf(slot[H * (D + 1) + j], f, L);
-            O = fmaf(slot[j * D + d], f, O);
+            const float mg = slot[H * D + j], lg = slot[H * (D + 1) + j], og = slot[j * D + d];
+            const float Mn = fmaxf(M, mg);
+            const float Mr = Mn == -INFINITY ? 0.f : Mn;
+            const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
+            L = fmaf(lg, f, L * a);
+            O = fmaf(og, f, O * a);
+            M = Mn;
         }
         E::store(p.out, (row_q0 + j) * D + d, L > 0.f ? O / L : 0.f);
     }
@@ -543,7 +524,7 @@ int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t 
 
 int launch_reduce_balanced(const AttnParams &p, int32_t dtype, int32_t head_dim, hipStream_t stream) {
 #define PKV_RED(E, D) \
-    hipLaunchKernelGGL((attn_reduce_balanced_kernel<E, D>), dim3(p.rows_per_seq, p.num_seqs), dim3(256), 0, stream, p)
+    hipLaunchKernelGGL((attn_reduce_balanced_kernel<E, D>), dim3(p.balanced_wgs), dim3(256), 0, stream, p)
     switch (dtype * 1000 + head_dim) {
     case PKV_F32 * 1000 + 64: PKV_RED(F32, 64); break;
     case PKV_F32 * 1000 + 128: PKV_RED(F32, 128); break;
@@ -579,7 +560,8 @@ int balanced_check(AttnParams &p) {
     const int cus = device_compute_units();
     if (cus <= 0) return fail(PKV_EHIP, "balanced partitioning: cannot read the device's compute-unit count");
     p.balanced_wgs = kBalancedWgsPerCu * cus;
-    const size_t need = static_cast<size_t>(2) * p.balanced_wgs * p.heads_per_row * (p.head_dim + 2) * sizeof(float);
+    const size_t need = static_cast<size_t>(2) * p.balanced_wgs * p.heads_per_row * (p.head_dim + 2) * sizeof(float) +
+                        (kBalancedMaxSeqs + 1) * sizeof(uint32_t) + static_cast<size_t>(2) * p.balanced_wgs * sizeof(int32_t);
     if (!p.ws || p.ws_bytes < need)
         return fail(PKV_EINVAL, "balanced partitioning: workspace of %zu bytes needed, %zu given", need, p.ws_bytes);
     return PKV_OK;
@@ -596,7 +578,8 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
         // two partial-result slots per workgroup, each for up to num_q_heads heads
         const int cus = device_compute_units();
         if (cus <= 0) return 0;
-        return static_cast<size_t>(2) * kBalancedWgsPerCu * cus * num_q_heads * (head_dim + 2) * sizeof(float);
+        return static_cast<size_t>(2) * kBalancedWgsPerCu * cus * num_q_heads * (head_dim + 2) * sizeof(float) +
+               (kBalancedMaxSeqs + 1) * sizeof(uint32_t) + static_cast<size_t>(2) * kBalancedWgsPerCu * cus * sizeof(int32_t);
     }
     if (partition_size <= 0) return 0;
     const int64_t parts = ceil_div(max_context_len, partition_size);

@@ -349,6 +349,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
     balanced_prefix<W * 64>(p, C, part);
+    balanced_zero_empty<E, 128, W * 64>(p, C);
     balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
         gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);

@@ -18,7 +18,7 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
     const char *__restrict__ key, const char *__restrict__ value, int64_t key_stride_b, int64_t value_stride_b,
     char *__restrict__ k_cache, char *__restrict__ v_cache, int64_t num_slots, const int64_t *__restrict__ slots,
-    int64_t total_chunks, int32_t chunks_per_row, int32_t num_kv_heads, int32_t block_size) {
+    int64_t total_chunks, int32_t chunks_per_row, int32_t num_kv_heads, int32_t block_size, int32_t block_shift) {
     const int32_t row_bytes = chunks_per_row * 16;
     const int64_t per_token = static_cast<int64_t>(chunks_per_row) * num_kv_heads;
     for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total_chunks;
@@ -27,13 +27,16 @@ __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
         const int32_t rem = static_cast<int32_t>(i - token * per_token);
         const int32_t h = rem / chunks_per_row;
         const int32_t c = rem - h * chunks_per_row;
-        const int64_t slot = slots[token];
-        if (slot < 0 || slot >= num_slots) continue;  // padding, or a slot outside the pool
-        const int64_t blk = slot / block_size;
-        const int64_t off = slot - blk * block_size;
-        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + c * 16;
+        // the token's rows and its slot are independent loads: all three are in flight together
+        // (the empty asm uses the rows here, so they are not moved behind the slot test)
         const u32x4 kv = *reinterpret_cast<const u32x4 *>(key + token * key_stride_b + h * row_bytes + c * 16);
         const u32x4 vv = *reinterpret_cast<const u32x4 *>(value + token * value_stride_b + h * row_bytes + c * 16);
+        const int64_t slot = slots[token];
+        asm volatile("" ::"v"(kv), "v"(vv));
+        if (slot < 0 || slot >= num_slots) continue;  // padding, or a slot outside the pool
+        const int64_t blk = block_shift >= 0 ? slot >> block_shift : slot / block_size;
+        const int64_t off = slot - blk * block_size;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + c * 16;
         *reinterpret_cast<u32x4 *>(k_cache + dst) = kv;
         *reinterpret_cast<u32x4 *>(v_cache + dst) = vv;
     }
@@ -90,7 +93,8 @@ extern "C" int pkv_reshape_and_cache(const void *key, const void *value, int64_t
     hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(kThreads), 0, stream,
                        static_cast<const char *>(key), static_cast<const char *>(value), key_stride * eb,
                        value_stride * eb, static_cast<char *>(k_cache), static_cast<char *>(v_cache),
-                       num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size);
+                       num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size,
+                       (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1);
     return hip_status(hipGetLastError(), "pkv_reshape_and_cache launch");
 }
 
