@@ -61,6 +61,15 @@ struct Mfma<F16> {
     static __device__ inline float value(unsigned short b) {
         return static_cast<float>(__builtin_bit_cast(_Float16, b));
     }
+    static __device__ inline unsigned pack2(float lo, float hi) {
+        const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};  // round to nearest even
+        return __builtin_bit_cast(unsigned, v);
+    }
+    // acc + the two packed values (exact products by one, fp32 accumulation)
+    static __device__ inline float sum2(unsigned packed, float acc) {
+        const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+    }
 };
 
 template <>
@@ -78,7 +87,26 @@ struct Mfma<BF16> {
         return __builtin_bit_cast(unsigned short, h);
     }
     static __device__ inline float value(unsigned short b) { return __uint_as_float(static_cast<unsigned>(b) << 16); }
+    static __device__ inline unsigned pack2(float lo, float hi) {
+        const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // round to nearest even
+        return __builtin_bit_cast(unsigned, v);
+    }
+    static __device__ inline float sum2(unsigned packed, float acc) {
+        const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+    }
 };
+
+// Max over lanes l, l^16, l^32, l^48 (the four lane groups), in every lane: permlane swaps,
+// no LDS round trip.
+__device__ inline float max_over_lane_groups(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // lanes l and l^32
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // lanes l and l^16
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 __device__ inline unsigned word(const u32x4 &r, int w) {
     return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
@@ -191,18 +219,22 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
             for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[u][kk], qv[kk], c);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool valid = S.ok[u] && (!tail || (S.in[u] && S.tok0[u] + 4 * g + i < t1));
-                sc[u][i] = valid ? c[i] * p.scale_log2 : -INFINITY;
+                sc[u][i] = c[i] * p.scale_log2;
+                if (tail) {
+                    const bool valid = S.ok[u] && S.in[u] && S.tok0[u] + 4 * g + i < t1;
+                    sc[u][i] = valid ? sc[u][i] : -INFINITY;
+                } else if (!S.ok[u]) {
+                    sc[u][i] = -INFINITY;
+                }
                 mloc = fmaxf(mloc, sc[u][i]);
             }
         }
-        // the head's running max over all four lane groups
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        // the head's running max over its four lane groups (lanes n, n+16, n+32, n+48)
+        mloc = max_over_lane_groups(mloc);
         const float m_new = fmaxf(m, mloc);
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        // rescale only when some head's max moved (uniform branch; alpha = 1 elsewhere)
-        if (__builtin_amdgcn_ballot_w64(m_new > m)) {
+        // rescale only when some head's max moved: rare after the first tiles (uniform branch)
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m) != 0, 0)) {
             const float alpha = fast_exp2(m - m_ref);
             lsum *= alpha;
 #pragma unroll
@@ -210,15 +242,12 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // P^T operand: head n, tokens 4g .. 4g+3 of tile u
-            unsigned short pb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pb[i] = M::bits(fast_exp2(sc[u][i] - m_ref));
-                lsum += M::value(pb[i]);
-            }
-            const u32x2 pt = {static_cast<unsigned>(pb[0]) | (static_cast<unsigned>(pb[1]) << 16),
-                              static_cast<unsigned>(pb[2]) | (static_cast<unsigned>(pb[3]) << 16)};
+            // P^T operand: head n, tokens 4g .. 4g+3 of tile u, rounded to the input type; the
+            // sum l takes the rounded weights (a dot2 with (1, 1) per pair)
+            const unsigned p01 = M::pack2(fast_exp2(sc[u][0] - m_ref), fast_exp2(sc[u][1] - m_ref));
+            const unsigned p23 = M::pack2(fast_exp2(sc[u][2] - m_ref), fast_exp2(sc[u][3] - m_ref));
+            lsum = M::sum2(p23, M::sum2(p01, lsum));
+            const u32x2 pt = {p01, p23};
             // (a rejected or stand-in tile reads as zeros and its weights are zero)
             // V^T operand of MFMA j: element j of the lane's 4 V rows
 #pragma unroll
