@@ -15,7 +15,7 @@ lengths; plus the new tokens' K/V read and written by reshape_and_cache.
 Helper modes (no GPU needed) turn rocprofv3 CSV output into the short text summaries kept
 under profiles/:
   bench.py --summarize-trace KERNEL_STATS_CSV OUT_TXT "COMMAND"
-  bench.py --summarize-counters FETCH_CSV WRITE_CSV OUT_TXT "FETCH_COMMAND" "WRITE_COMMAND"
+  bench.py --summarize-counters WORKLOAD_NAME FETCH_CSV WRITE_CSV OUT_TXT "FETCH_COMMAND" "WRITE_COMMAND"
 """
 import argparse
 import csv
@@ -33,16 +33,23 @@ METRIC = "paged decode attention: KV GB/s (% HBM peak) and decode tokens/s, 13B 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
 PARTITION_BALANCED = -1  # the library's balanced split mode
 FLAG_CACHED_KV = 2  # the library's cached K/V load flag
-ATTN_SOURCES = ["paged_kv_cache_416_amd/csrc/attention.hip", "paged_kv_cache_416_amd/csrc/attention.h",
-                "paged_kv_cache_416_amd/csrc/common.h"]
 PROFILES = os.path.join(ROOT, "profiles")
-# attention kernel name prefix -> counters summary for the default workload
-COUNTERS_FILE = {"13b-decode": "attn_decode_f16_13b_counters.txt"}
+CSRC = "paged_kv_cache_416_amd/csrc/"
+# workload -> (counter summary under profiles/, sources of its attention kernel, kernel name part,
+#              partition size and flags the summary was taken at)
+COUNTERS = {
+    "13b-decode": ("attn_decode_f16_13b_counters.txt",
+                   [CSRC + "attention.hip", CSRC + "attention.h", CSRC + "common.h"],
+                   "attn_decode_kernel", 0, 0),
+    "8b-gqa-prefix": ("attn_gqa_bf16_8b_balanced_counters.txt",
+                      [CSRC + "attention_gqa.hip", CSRC + "attention.h", CSRC + "common.h"],
+                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, FLAG_CACHED_KV),
+}
 
 
-def attn_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -87,7 +94,8 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain elementwise kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "CMD"))
-    ap.add_argument("--summarize-counters", nargs=5, metavar=("FETCH_CSV", "WRITE_CSV", "OUT", "CMD1", "CMD2"))
+    ap.add_argument("--summarize-counters", nargs=6,
+                    metavar=("WORKLOAD_NAME", "FETCH_CSV", "WRITE_CSV", "OUT", "CMD1", "CMD2"))
     return ap.parse_args()
 
 
@@ -105,6 +113,16 @@ def make_workload(name):
     raise ValueError(name)
 
 
+def kernel_label(w, P, flags):
+    """Names of the kernels one attention call launches (the library's dispatch rule)."""
+    g = w.num_q_heads // w.num_kv_heads
+    mfma = (g > 1 and w.dtype in ("f16", "bf16") and w.head_dim == 128 and w.block_size in (16, 32)
+            and g <= 16 and not flags & 1)
+    if P == PARTITION_BALANCED:
+        return ("attn_gqa_balanced_kernel" if mfma else "attn_decode_balanced_kernel") + "+attn_reduce_balanced_kernel"
+    return ("attn_gqa_mfma_kernel" if mfma else "attn_decode_kernel") + ("+attn_reduce_kernel" if P > 0 else "")
+
+
 def timed_launches(fn, n, stream):
     """Average device time of one launch of fn(i): HIP events on the launch stream around n
     back-to-back launches (the gaps between them included)."""
@@ -118,12 +136,14 @@ def timed_launches(fn, n, stream):
     return 1e3 * a.elapsed_time(b) / n
 
 
-def read_counters(workload):
+def read_counters(workload, P, flags):
     """Measured HBM bytes per attention launch from the committed counter summary, if it was
-    taken on the attention source as it is now; else None."""
-    name = COUNTERS_FILE.get(workload)
-    path = os.path.join(PROFILES, name) if name else None
-    if not path or not os.path.exists(path):
+    taken at this partition size and flags on the kernel source as it is now; else None."""
+    entry = COUNTERS.get(workload)
+    if entry is None or (P, flags) != (entry[3], entry[4]):
+        return None
+    path = os.path.join(PROFILES, entry[0])
+    if not os.path.exists(path):
         return None
     kv = {}
     with open(path) as fh:
@@ -131,7 +151,7 @@ def read_counters(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != attn_source_hash():
+    if kv.get("kernel_source_sha256") != source_hash(entry[1]):
         return None
     return float(kv["traffic_bytes_per_dispatch"])
 
@@ -213,7 +233,7 @@ def main():
 
     value = (unique_b + w_bytes) / (ms_per_step * 1e-3) / 1e9
     achieved = unique_b / (attn_us * 1e-6) / 1e9
-    traffic = read_counters(w.name) if P == 0 and flags == 0 else None
+    traffic = read_counters(w.name, P, flags)
 
     result = {
         "metric": METRIC,
@@ -238,8 +258,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": round(traffic) if traffic is not None else None,
-                     "kernel": "attn_decode_kernel" + ("+attn_reduce_kernel" if P > 0 else "")
-                               + ("(balanced)+attn_reduce_balanced_kernel" if P == PARTITION_BALANCED else "")},
+                     "kernel": kernel_label(w, P, flags)},
     }
 
     if args.copy_probe:
@@ -340,7 +359,7 @@ def summarize_trace(stats_csv, out, cmd):
     print("\n".join(lines))
 
 
-def summarize_counters(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
+def summarize_counters(workload, fetch_csv, write_csv, out, cmd_fetch, cmd_write):
     """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) -> HBM bytes per attention
     launch, each counter scaled by what it reads for a plain elementwise kernel over a known size."""
     def per_kernel(path):
@@ -351,7 +370,8 @@ def summarize_counters(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     probe = [k for k in fetch if "neg_kernel" in k]
-    attn = [k for k in fetch if "attn_decode_kernel" in k]
+    _, sources, kname, _, _ = COUNTERS[workload]
+    attn = [k for k in fetch if kname in k]
     if len(probe) != 1 or len(attn) != 1:
         raise SystemExit(f"expected one probe and one attention kernel, got {probe} / {attn}")
     probe_bytes = 1 << 30  # --copy-probe 1024: 1 GiB read, 1 GiB written
@@ -366,7 +386,7 @@ def summarize_counters(fetch_csv, write_csv, out, cmd_fetch, cmd_write):
              "# scale = bytes the calibration kernel (torch.neg over 1 GiB: 1 GiB read, 1 GiB written) moved,",
              "#         divided by what the counter reported for it",
              f"kernel: {_short(attn[0])}",
-             f"kernel_source_sha256: {attn_source_hash()}",
+             f"kernel_source_sha256: {source_hash(sources)}",
              f"dispatches: {len(fetch[attn[0]])}",
              f"fetch_kib_per_dispatch: {af:.1f}",
              f"write_kib_per_dispatch: {aw:.1f}",
