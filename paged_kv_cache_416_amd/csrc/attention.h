@@ -330,8 +330,9 @@ int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t 
 int launch_reduce_balanced(const AttnParams &p, int32_t dtype, int32_t head_dim, hipStream_t stream);
 // Compute units of the current device (cached), or -1.
 int device_compute_units();
-// Sets p.balanced_wgs and checks the balanced schedule's limits and workspace (p.tile_rows and
-// p.heads_per_row set by the caller).
-int balanced_check(AttnParams &p);
+// Sets p.balanced_wgs (wgs_per_cu workgroups per compute unit, at most kBalancedWgsPerCu) and
+// checks the balanced schedule's limits and workspace (p.tile_rows and p.heads_per_row set by
+// the caller).
+int balanced_check(AttnParams &p, int wgs_per_cu = kBalancedWgsPerCu);
 
 }  // namespace pkv

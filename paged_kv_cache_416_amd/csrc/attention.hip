@@ -552,14 +552,14 @@ int device_compute_units() {
     return n;
 }
 
-int balanced_check(AttnParams &p) {
+int balanced_check(AttnParams &p, int wgs_per_cu) {
     if (p.num_seqs > kBalancedMaxSeqs)
         return fail(PKV_EUNSUPPORTED, "balanced partitioning: %d sequences, at most %d", p.num_seqs, kBalancedMaxSeqs);
     const int64_t tiles = static_cast<int64_t>(p.num_seqs) * ceil_div(p.ctx_cap, p.tile_rows);
     if (tiles >= (int64_t(1) << 31)) return fail(PKV_EINVAL, "balanced partitioning: %lld tiles per row", (long long)tiles);
     const int cus = device_compute_units();
     if (cus <= 0) return fail(PKV_EHIP, "balanced partitioning: cannot read the device's compute-unit count");
-    p.balanced_wgs = kBalancedWgsPerCu * cus;
+    p.balanced_wgs = wgs_per_cu * cus;
     const size_t need = static_cast<size_t>(2) * p.balanced_wgs * p.heads_per_row * (p.head_dim + 2) * sizeof(float) +
                         (kBalancedMaxSeqs + 1) * sizeof(uint32_t) + static_cast<size_t>(2) * p.balanced_wgs * sizeof(int32_t);
     if (!p.ws || p.ws_bytes < need)

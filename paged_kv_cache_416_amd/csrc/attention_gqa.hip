@@ -37,8 +37,10 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGqaWaves = 4;
-constexpr int kGqaTiles = 1;  // tiles per stage
+constexpr int kGqaWaves = 4;          // per-item schedule: two workgroups per CU
+constexpr int kGqaBalancedWaves = 8;  // balanced schedule: one workgroup per CU (two waves per SIMD)
+constexpr int kGqaTiles = 1;   // tiles per stage
+constexpr int kGqaStages = 2;  // stages in flight + the one consumed
 constexpr int kMaxGroup = 16;
 
 template <class E>
@@ -118,10 +120,19 @@ struct GqaLds {
     float acc[W][kMaxGroup][128];
 };
 
+// Table entries as scalar loads: the constant address space (the tables are not written while
+// a kernel runs) with a uniform index gives s_load, whose completion counter is not the one the
+// K/V loads use, so looking an entry up never waits for K/V data.
+typedef const __attribute__((address_space(4))) int32_t TableEntry;
+
 // Tokens [t0, t1) of sequence s for kv head kvh and its G query heads (t0 a multiple of 16,
 // t0 < t1 <= the length): the workgroup's merged result goes to sink. Uniform over the
 // workgroup; ends with a barrier, so the caller may run it again on the same LDS. head_dim 128,
-// 16-bit types; U tiles per stage, stages double-buffered in registers.
+// 16-bit types.
+//
+// The range's tiles go to the waves in stages of U tiles, round-robin. Each wave keeps NS
+// stages in registers: while it consumes one, the next NS - 1 are in flight, and the table
+// entries of the stage after those are on the way.
 template <class E, int B, bool PAGED, int W, int U, bool NT>
 __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
                                  GqaLds<W> &lds) {
@@ -130,23 +141,19 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     constexpr int TR = 16;          // tile rows
     constexpr int SPB = B / TR;     // tiles per block
     constexpr int ROWB = D * 2;     // bytes per row
+    constexpr int NS = kGqaStages;
     static_assert(B % TR == 0, "block_size must be a multiple of 16");
-    static_assert(64 % U == 0, "a stage must not straddle a table chunk");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers, scalar branches
     const int G = p.group;
     const int n = lane & 15, g = lane >> 4;
     const int jt0 = t0 / TR;
+    const int ntile = (t1 + TR - 1) / TR - jt0;
+    const int nstage = (ntile + U - 1) / U;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
-
-    const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
-    int tb = 0;
-    auto fetch_table = [&](int base) -> int {
-        const int j = (jt0 + wave + (base + lane) * W) / SPB;
-        return j < p.max_blocks ? trow[j] : 0;
-    };
-    if constexpr (PAGED) tb = fetch_table(0);
+    TableEntry *trow = PAGED ? (TableEntry *)(p.tables + static_cast<int64_t>(s) * p.max_blocks)  // address-space cast
+                             : nullptr;
 
     // Q^T operand: query head n of the group, chunks 4*kk + g; zero for n >= G.
     u32x4 qv[4];
@@ -159,49 +166,56 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
-    const int ntile = (t1 + TR - 1) / TR - jt0;
-    const int nk = ntile > wave ? (ntile - wave + W - 1) / W : 0;
 
-    auto tile_offset = [&](int k, int kc0, bool &ok) -> int64_t {
-        const int jt = jt0 + wave + k * W;
-        if constexpr (PAGED) {
-            const int pb = __builtin_amdgcn_readlane(tb, k - kc0);
-            ok = static_cast<uint32_t>(pb) < p.num_blocks;  // 32-bit, so it stays a scalar compare
-            const int64_t blk = ok ? pb : 0;
-            return ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
-        } else {
-            ok = true;
-            return ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
+    // the next stage this wave will issue (wave w takes stages w, w + W, w + 2W, ...: a fixed
+    // assignment, so the summation order and the result do not depend on timing) and its
+    // table entries, looked up one stage ahead
+    int cst = wave;
+    int cpb[U];
+    auto lookup = [&]() {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = min(cst * U + u, ntile - 1);  // a stand-in past the range reads the last entry
+            cpb[u] = PAGED ? trow[(jt0 + k) / SPB] : 0;
         }
     };
+    lookup();
 
     struct Stage {
         u32x4 k[U][4], v[U][4];
-        int tok0[U];
+        int st;      // stage index within the range (>= nstage: a stand-in)
         bool ok[U];  // table entry inside the pool
-        bool in[U];  // tile belongs to this wave (false: a stand-in, masked out)
     };
 
     // Every load is unconditional (exact wait counts) and goes through a buffer resource that
-    // ends at the tile's last row inside [t0, t1): rows past it, a tile past the wave's last
-    // (clamp) and a tile whose table entry is rejected read as zeros; consume() masks them out.
+    // ends at the tile's last row inside [t0, t1): rows past it, a stand-in tile and a tile whose
+    // table entry is rejected read as zeros, with no memory traffic; consume() masks them out.
     const unsigned koff = n * ROWB + g * 16;      // + kk * 64: row n, chunk 4*kk + g
     const unsigned voff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n
-    auto issue = [&](Stage &S, int kc0, int st, bool clamp) {
+    auto issue = [&](Stage &S) {
+        S.st = cst;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int k = kc0 + st * U + u;
-            S.in[u] = k < nk;
-            const int kr = clamp ? min(k, nk - 1) : k;  // table lane to read
-            const int64_t tile = tile_offset(kr, kc0, S.ok[u]);
-            S.tok0[u] = (jt0 + wave + k * W) * TR;
-            const int rows = S.in[u] && S.ok[u] ? min(TR, t1 - S.tok0[u]) : 0;
+            const int k = cst * U + u;
+            const int jt = jt0 + min(k, ntile - 1);
+            int64_t tile;
+            if constexpr (PAGED) {
+                S.ok[u] = static_cast<uint32_t>(cpb[u]) < p.num_blocks;  // 32-bit, so it stays a scalar compare
+                const int64_t blk = S.ok[u] ? cpb[u] : 0;
+                tile = ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
+            } else {
+                S.ok[u] = true;
+                tile = ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
+            }
+            const int rows = k < ntile && S.ok[u] ? min(TR, t1 - (jt0 + k) * TR) : 0;
             const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) S.k[u][kk] = kv_buffer_load<NT>(kr_, koff + kk * 64);
 #pragma unroll
             for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<NT>(vr_, voff + i * ROWB);
         }
+        cst += W;
+        lookup();
     };
 
     float m = -INFINITY, lsum = 0.f;
@@ -209,7 +223,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto consume = [&](Stage &S, bool tail) {
+    auto consume = [&](Stage &S) {
         float sc[U][4];
         float mloc = -INFINITY;
 #pragma unroll
@@ -217,15 +231,11 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[u][kk], qv[kk], c);
+            const int tok0 = (jt0 + S.st * U + u) * TR;  // a stand-in's rows all lie past t1
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sc[u][i] = c[i] * p.scale_log2;
-                if (tail) {
-                    const bool valid = S.ok[u] && S.in[u] && S.tok0[u] + 4 * g + i < t1;
-                    sc[u][i] = valid ? sc[u][i] : -INFINITY;
-                } else if (!S.ok[u]) {
-                    sc[u][i] = -INFINITY;
-                }
+                const bool valid = S.ok[u] && tok0 + 4 * g + i < t1;
+                sc[u][i] = valid ? c[i] * p.scale_log2 : -INFINITY;
                 mloc = fmaxf(mloc, sc[u][i]);
             }
         }
@@ -262,42 +272,25 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         m = m_new;
     };
 
-    // The wave's tiles in chunks of 64 (one table register each); stages of U tiles are
-    // double-buffered; only a wave's last stages need clamping and masks.
-    for (int kc0 = 0; kc0 < nk; kc0 += 64) {
-        if constexpr (PAGED) {
-            if (kc0 > 0) tb = fetch_table(kc0);
-        }
-        const int nst = (min(64, nk - kc0) + U - 1) / U;
-        const bool last_chunk = kc0 + 64 >= nk;
-        Stage A, Bs;
-        int st = 0;
-        issue(A, kc0, 0, last_chunk && nst < 2);
-        while (st + 4 <= nst) {
-            issue(Bs, kc0, st + 1, false);
-            consume(A, false);
+    // A ring of NS stages; the wave stops once the oldest stage is past the range (its later
+    // stages are stand-ins too).
+    Stage R[NS];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) {
+        issue(R[i]);  // in order: the first stage's loads return first
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Whole rounds of NS stages, the test for the end only at a round's start: straight-line
+    // rounds keep the compiler's wait counts exact. The last round may consume up to NS - 1
+    // stand-ins (zeros, masked; their loads move no data).
+    for (;;) {
+        if (R[0].st >= nstage) break;
+#pragma unroll
+        for (int r = 0; r < NS; ++r) {
+            issue(R[(r + NS - 1) % NS]);
+            consume(R[r]);
             __builtin_amdgcn_sched_barrier(0);
-            issue(A, kc0, st + 2, false);
-            consume(Bs, false);
-            __builtin_amdgcn_sched_barrier(0);
-            st += 2;
-        }
-        switch (nst - st) {
-        case 1:
-            consume(A, true);
-            break;
-        case 2:
-            issue(Bs, kc0, st + 1, true);
-            consume(A, true);
-            consume(Bs, true);
-            break;
-        default:
-            issue(Bs, kc0, st + 1, true);
-            consume(A, true);
-            issue(A, kc0, st + 2, true);
-            consume(Bs, true);
-            consume(A, true);
-            break;
         }
     }
 
@@ -369,8 +362,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, t0, t1, sink, lds);
 }
 
-// Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
-// (work rows = (kv head, sequence), head-major); cut rows are merged by the balanced reduce pass.
+// Balanced schedule: grid = balanced_wgs workgroups (one per CU), each an equal share of the
+// batch's tiles (work rows = (kv head, sequence), head-major); cut rows are merged by the
+// balanced reduce pass. One workgroup per CU because two sharing a CU do not progress at one
+// pace (the older one's waves are served first), and the later one would finish alone.
 template <class E, int B, bool PAGED, int W, int U, bool NT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
     const AttnParams p) {
@@ -393,10 +388,10 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
         q.rows_per_seq = p.num_kv_heads;
         q.heads_per_row = p.group;
         q.head_major = 1;  // an XCD's shares cover few kv heads: shared blocks stay in its L2
-        int rc = balanced_check(q);
+        int rc = balanced_check(q, 1);  // one workgroup per CU: two per CU would not run at one pace
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, NT>), dim3(q.balanced_wgs),
-                           dim3(kGqaWaves * 64), 0, stream, q);
+        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaBalancedWaves, kGqaTiles, NT>),
+                           dim3(q.balanced_wgs), dim3(kGqaBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "grouped-query attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
     }
