@@ -142,7 +142,9 @@ int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t
  *  slot_mapping: device int64[num_tokens]; a negative slot is skipped (padding).
  * Byte-exact copy. Slots >= num_blocks*block_size are skipped by the kernel (a caller
  * error). Duplicate non-negative slots in one call are a caller error (result
- * unspecified). Pointers must be 16-byte aligned and strides*elt multiples of 16. */
+ * unspecified); with PKV_DEBUG_VALIDATE=1 both are PKV_EINVAL, launching nothing
+ * (slot_mapping copied to the host after the stream's earlier work). Pointers must be
+ * 16-byte aligned and strides*elt multiples of 16. */
 int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride, int64_t value_stride,
                           void *k_cache, void *v_cache, int64_t num_blocks, const int64_t *slot_mapping,
                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -188,6 +190,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  * Device-side guards (never faults on bad tables, but the result is then unspecified):
  * lengths are clamped to [0, min(max_context_len, max_blocks_per_seq*block_size)] and a
  * table entry outside [0, num_blocks) contributes no tokens.
+ * With the environment variable PKV_DEBUG_VALIDATE=1 the call first copies context_lens and
+ * block_tables to the host (synchronising the stream; not for graph capture) and returns
+ * PKV_EINVAL, launching nothing, for a length outside [0, max_context_len], a length needing
+ * more than max_blocks_per_seq blocks, a used table entry outside [0, num_blocks), or an array
+ * that is not device memory.
  * Supported: dtype f32/f16/bf16; head_dim 64 or 128; block_size 8, 16 or 32;
  * num_q_heads a multiple of num_kv_heads. */
 int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -200,12 +207,26 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
 /* The same attention over a contiguous cache, the layout paging replaces (slide 19 prices
  * the indirection against it): k, v are [num_seqs][num_kv_heads][lmax][head_dim] and token t
  * of (s, kv head) is row t of that slab. Same kernels, same tiling; only the address of a
- * tile differs. Lengths are clamped to [0, min(max_context_len, lmax)]. */
+ * tile differs. Lengths are clamped to [0, min(max_context_len, lmax)]; with
+ * PKV_DEBUG_VALIDATE=1 a length above either is PKV_EINVAL (context_lens copied to the host). */
 int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, const void *v, int32_t lmax,
                                     const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float scale,
                                     int32_t partition_size, void *workspace, size_t workspace_bytes,
                                     int32_t dtype, uint32_t flags, hipStream_t stream);
+
+/* ======================================================================
+ * Measurement companion (not part of the method).
+ * ==================================================================== */
+
+/* Read `bytes` of device memory at src once, with the 16-byte non-temporal loads the attention
+ * kernels use, and nothing else: timing it gives the device's achievable streaming-read rate,
+ * the context for an attention GB/s figure next to the datasheet HBM peak.
+ *  src: device, 16-byte aligned; bytes a multiple of 16.
+ *  sink: device, 16-byte aligned, 4 bytes; written only in the (practically impossible) case
+ *        that the buffer's XOR-fold equals 0x9e3779b9, which keeps the loads live.
+ * PKV_EINVAL for NULL or misaligned arguments. */
+int pkv_read_probe(const void *src, size_t bytes, void *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -47,6 +47,7 @@ SIGNATURES = {
                                                   _i32, _f32, _i32, _p, _sz, _i32, _u32, _p]),
     "pkv_contiguous_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                                        _f32, _i32, _p, _sz, _i32, _u32, _p]),
+    "pkv_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),
 }
 
 _lib = None

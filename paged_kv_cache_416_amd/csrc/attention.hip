@@ -606,6 +606,11 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (!block_tables || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "%s: block_tables NULL or max_blocks_per_seq / num_blocks not positive", fn);
     if (num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: num_blocks %lld exceeds int32", fn, (long long)num_blocks);
+    if (debug_validate()) {
+        rc = validate_attention(fn, context_lens, num_seqs, max_context_len, block_tables, max_blocks_per_seq,
+                                block_size, num_blocks, 0, stream);
+        if (rc) return rc;
+    }
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
     AttnParams p = make_params(out, q, k_cache, v_cache, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
                                partition_size, max_context_len, static_cast<int32_t>(cap), workspace,
@@ -632,6 +637,10 @@ extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const v
     // tile rows of the contiguous slab: 16 (any multiple of rows-per-load works)
     constexpr int32_t kTile = 16;
     if (partition_size > 0 && partition_size % kTile) return fail(PKV_EINVAL, "%s: partition_size must be a multiple of 16", fn);
+    if (debug_validate()) {
+        rc = validate_attention(fn, context_lens, num_seqs, max_context_len, nullptr, 0, 0, 0, lmax, stream);
+        if (rc) return rc;
+    }
     const int32_t cap = std::min(max_context_len, lmax);
     AttnParams p = make_params(out, q, k, v, context_lens, num_seqs, num_q_heads, num_kv_heads, scale,
                                partition_size, max_context_len, cap, workspace, workspace_bytes, head_dim);

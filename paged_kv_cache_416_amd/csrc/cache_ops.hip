@@ -86,6 +86,10 @@ extern "C" int pkv_reshape_and_cache(const void *key, const void *value, int64_t
     if ((key_stride * eb) % 16 || (value_stride * eb) % 16 || !aligned16(key) || !aligned16(value) ||
         !aligned16(k_cache) || !aligned16(v_cache))
         return fail(PKV_EINVAL, "pkv_reshape_and_cache: pointers and strides must be 16-byte aligned");
+    if (debug_validate()) {
+        const int rc = validate_slots("pkv_reshape_and_cache", slot_mapping, num_tokens, num_blocks * block_size, stream);
+        if (rc) return rc;
+    }
     const int32_t cpr = static_cast<int32_t>(row_bytes / 16);
     const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * cpr;
     const int64_t want = ceil_div(total, kThreads);

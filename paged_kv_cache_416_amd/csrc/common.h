@@ -24,4 +24,19 @@ inline int elt_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
 inline bool valid_dtype(int32_t dtype) { return dtype == PKV_F32 || dtype == PKV_F16 || dtype == PKV_BF16; }
 
+// PKV_DEBUG_VALIDATE set (and not "0"): the entry points check the device-side contract on
+// host copies before launching.
+bool debug_validate();
+
+// Lengths within [0, max_context_len] (and lmax when block_tables is NULL: the contiguous
+// layout), at most max_blocks blocks, every used table entry inside [0, num_blocks).
+// Synchronises `stream`; PKV_EINVAL with a message on the first violation.
+int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                       const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
+                       int32_t lmax, hipStream_t stream);
+
+// Slots below num_slots and no non-negative slot twice. Synchronises `stream`.
+int validate_slots(const char *fn, const int64_t *slot_mapping, int32_t num_tokens, int64_t num_slots,
+                   hipStream_t stream);
+
 }  // namespace pkv

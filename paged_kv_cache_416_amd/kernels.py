@@ -130,3 +130,12 @@ def contiguous_attention_decode(out, q, k, v, context_lens, max_context_len, sca
                                                  int(partition_size), _ptr(workspace), ws_bytes,
                                                  dtype_code(q.dtype), int(flags), _stream()))
     return out
+
+
+def read_probe(src, sink):
+    """Read all of src (a contiguous device tensor, size a multiple of 16 bytes) once; sink is a
+    device tensor of at least 4 bytes (the probe's liveness sink)."""
+    _need_cuda(src, sink)
+    if not src.is_contiguous() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("src must be contiguous and sink at least 4 bytes")
+    check(load().pkv_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream()))

@@ -147,3 +147,11 @@ def test_gpu_calls_fail_loudly_without_a_device():
     rc = lib.pkv_reshape_and_cache(FAKE, FAKE, 512, 512, FAKE, FAKE, 4, slots.ctypes.data_as(ctypes.c_void_p), 1, 4,
                                    128, 16, 1, NULL)
     assert rc == _lib.PKV_EHIP
+
+
+def test_read_probe_rejects_bad_arguments():
+    lib = _lib.load()
+    assert lib.pkv_read_probe(NULL, 1024, FAKE, NULL) == _lib.PKV_EINVAL
+    assert lib.pkv_read_probe(FAKE, 1000, FAKE, NULL) == _lib.PKV_EINVAL  # not a multiple of 16
+    assert lib.pkv_read_probe(ctypes.c_void_p((1 << 20) + 8), 1024, FAKE, NULL) == _lib.PKV_EINVAL
+    assert lib.pkv_read_probe(FAKE, 0, FAKE, NULL) == _lib.PKV_OK

@@ -1,0 +1,99 @@
+"""PKV_DEBUG_VALIDATE=1: the entry points check the device-side contract on host copies and
+reject a violation with PKV_EINVAL before launching anything (the bad inputs below never reach
+a kernel). Valid inputs give the same bytes as without the check."""
+import pytest
+import torch
+
+from paged_kv_cache_416_amd import kernels
+from paged_kv_cache_416_amd._lib import PKV_EINVAL, PkvError
+
+pytestmark = pytest.mark.gpu
+
+N, HKV, HQ, B, D = 8, 2, 4, 16, 64
+
+
+def _setup():
+    g = torch.Generator().manual_seed(7)
+    dev = torch.device("cuda")
+    k = (torch.randn(N, HKV, B, D, generator=g) * 0.5).half().to(dev)
+    v = (torch.randn(N, HKV, B, D, generator=g) * 0.5).half().to(dev)
+    q = (torch.randn(2, HQ, D, generator=g) * 0.5).half().to(dev)
+    tables = torch.tensor([[3, 1, -1], [6, 0, 5]], dtype=torch.int32, device=dev)
+    ctx = torch.tensor([20, 40], dtype=torch.int32, device=dev)
+    return k, v, q, tables, ctx
+
+
+def _attend(k, v, q, tables, ctx, max_ctx=48):
+    out = torch.empty_like(q)
+    kernels.paged_attention_decode(out, q, k, v, tables, ctx, max_ctx, D ** -0.5)
+    torch.cuda.synchronize()
+    return out
+
+
+def _rejects(fn, *args, match):
+    with pytest.raises(PkvError) as e:
+        fn(*args)
+    assert e.value.code == PKV_EINVAL and match in str(e.value) and "PKV_DEBUG_VALIDATE" in str(e.value)
+
+
+def test_valid_inputs_pass_and_give_the_same_bytes(monkeypatch):
+    k, v, q, tables, ctx = _setup()
+    plain = _attend(k, v, q, tables, ctx)
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    checked = _attend(k, v, q, tables, ctx)
+    assert torch.equal(plain.view(torch.int16), checked.view(torch.int16))
+    # an entry past a sequence's last block is never used, so it is not checked
+    tables[0, 2] = 1 << 20
+    _attend(k, v, q, tables, ctx)
+
+
+def test_used_table_entry_outside_the_pool(monkeypatch):
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    k, v, q, tables, ctx = _setup()
+    tables[1, 2] = N
+    _rejects(_attend, k, v, q, tables, ctx, match="block_tables[1][2]")
+    tables[1, 2] = -3
+    _rejects(_attend, k, v, q, tables, ctx, match="block_tables[1][2]")
+
+
+def test_length_above_max_context_len_or_table(monkeypatch):
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    k, v, q, tables, ctx = _setup()
+    ctx[0] = 49
+    _rejects(_attend, k, v, q, tables, ctx, 48, match="context_lens[0]")
+    ctx[0] = 49  # 4 blocks, the table holds 3
+    _rejects(_attend, k, v, q, tables, ctx, 64, match="needs 4 blocks")
+    ctx[0] = -1
+    _rejects(_attend, k, v, q, tables, ctx, match="context_lens[0]")
+
+
+def test_contiguous_length_above_lmax(monkeypatch):
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    k, v, q, tables, ctx = _setup()
+    kc = torch.zeros(2, HKV, 32, D, dtype=torch.half, device="cuda")
+    out = torch.empty_like(q)
+    ok = torch.tensor([32, 5], dtype=torch.int32, device="cuda")
+    kernels.contiguous_attention_decode(out, q, kc, kc, ok, 32, D ** -0.5)
+    bad = torch.tensor([32, 33], dtype=torch.int32, device="cuda")
+    _rejects(kernels.contiguous_attention_decode, out, q, kc, kc, bad, 64, D ** -0.5, match="exceeds lmax")
+
+
+def test_reshape_and_cache_slots(monkeypatch):
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    k, v, q, tables, ctx = _setup()
+    key = torch.randn(3, HKV, D, device="cuda").half()
+    val = torch.randn(3, HKV, D, device="cuda").half()
+    before = k.clone()
+    kernels.reshape_and_cache(key, val, k, v, torch.tensor([5, -1, 17], dtype=torch.int64, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(k[0, :, 5], key[0]) and torch.equal(k[1, :, 1], key[2])
+    dup = torch.tensor([9, 40, 9], dtype=torch.int64, device="cuda")
+    _rejects(kernels.reshape_and_cache, key, val, k, v, dup, match="appears twice")
+    far = torch.tensor([9, N * B, 3], dtype=torch.int64, device="cuda")
+    _rejects(kernels.reshape_and_cache, key, val, k, v, far, match="slot_mapping[1]")
+    torch.cuda.synchronize()
+    # the rejected calls wrote nothing
+    after = k.clone()
+    after[0, :, 5] = before[0, :, 5]
+    after[1, :, 1] = before[1, :, 1]
+    assert torch.equal(after, before)
