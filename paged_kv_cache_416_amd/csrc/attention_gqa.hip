@@ -21,8 +21,9 @@
 //  * the output tile leaves head n and d = 8(4g + i) + j in lane l, so the online-softmax
 //    rescale of a head is lane-local; only the running max crosses the four lane groups, and
 //    the rescale is skipped when no head's max moved.
-// The softmax weights enter the second MFMA rounded to the input type (the sum l is taken over
-// the same rounded weights, so the output is an exact convex combination of them).
+// The softmax weights enter the second contraction as two 16-bit parts each (the rounded
+// weight and its rounded remainder), so that contraction sees them to about 2^-16 relative,
+// and the sum l is taken over the same parts.
 // Loads, table handling, double buffering, masking and the split workspace are as in the
 // one-head kernel. The grid is (kv heads, partitions, sequences) with the kv head fastest, so a
 // kv head's workgroups land on the same XCDs and a shared prefix stays in their L2.
@@ -252,12 +253,18 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // P^T operand: head n, tokens 4g .. 4g+3 of tile u, rounded to the input type; the
-            // sum l takes the rounded weights (a dot2 with (1, 1) per pair)
-            const unsigned p01 = M::pack2(fast_exp2(sc[u][0] - m_ref), fast_exp2(sc[u][1] - m_ref));
-            const unsigned p23 = M::pack2(fast_exp2(sc[u][2] - m_ref), fast_exp2(sc[u][3] - m_ref));
-            lsum = M::sum2(p23, M::sum2(p01, lsum));
-            const u32x2 pt = {p01, p23};
+            // P^T operand: head n, tokens 4g .. 4g+3 of tile u. The matrix cores take 16-bit
+            // operands, so each weight goes in as a 16-bit part plus the 16-bit rounding of its
+            // remainder (the remainder of a round to nearest is exact in fp32): two contractions
+            // see the fp32 weight to about 2^-16 relative. The sum l takes the same parts (a dot2
+            // with (1, 1) per pair).
+            const float e0 = fast_exp2(sc[u][0] - m_ref), e1 = fast_exp2(sc[u][1] - m_ref);
+            const float e2 = fast_exp2(sc[u][2] - m_ref), e3 = fast_exp2(sc[u][3] - m_ref);
+            const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
+            const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
+            const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
+            lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
+            const u32x2 ph = {h01, h23}, pr = {r01, r23};
             // (a rejected or stand-in tile reads as zeros and its weights are zero)
             // V^T operand of MFMA j: element j of the lane's 4 V rows
 #pragma unroll
@@ -266,7 +273,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
                 const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
                 const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[u][1], w), word(S.v[u][0], w), sel),
                                   __builtin_amdgcn_perm(word(S.v[u][3], w), word(S.v[u][2], w), sel)};
-                acc[j] = M::mma16(vt, pt, acc[j]);
+                acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
             }
         }
         m = m_new;

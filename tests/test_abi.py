@@ -155,3 +155,8 @@ def test_read_probe_rejects_bad_arguments():
     assert lib.pkv_read_probe(FAKE, 1000, FAKE, NULL) == _lib.PKV_EINVAL  # not a multiple of 16
     assert lib.pkv_read_probe(ctypes.c_void_p((1 << 20) + 8), 1024, FAKE, NULL) == _lib.PKV_EINVAL
     assert lib.pkv_read_probe(FAKE, 0, FAKE, NULL) == _lib.PKV_OK
+
+
+def test_balanced_split_refuses_more_than_4096_sequences():
+    assert _attn(S=4097, P=-1) == _lib.PKV_EUNSUPPORTED
+    assert "4096" in _lib.load().pkv_last_error().decode()
