@@ -24,12 +24,27 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what=""):
+# significand bits of each output type (the implicit bit included)
+_PRECISION = {"f32": 24, "f16": 11, "bf16": 8}
+
+
+def output_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """One unit in the last place of the output type at |ref| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-30)))
+    return np.exp2(e - (_PRECISION[dtype] - 1))
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what="", storage_ulp=False):
+    """|gpu - ref| <= tol + tol*|ref| element by element; with storage_ulp, plus one unit in the
+    last place of the output type (for outputs so large that storing them in a 16-bit type
+    alone can exceed the relative tolerance: bf16 above |o| of about 1)."""
     g = to_f64(got)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     tol = TOL[dtype]
     err = np.abs(g - ref)
     bound = tol + tol * np.abs(ref)
+    if storage_ulp:
+        bound = bound + output_ulp(ref, dtype)
     bad = ~(err <= bound)
     if bad.any():
         i = np.unravel_index(np.argmax(np.where(bad, err - bound, -np.inf)), ref.shape)
