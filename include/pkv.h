@@ -121,6 +121,23 @@ int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32
 int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_tokens, int32_t n_seqs,
                    int64_t *slots_out, int32_t *cow_pairs_out, int32_t max_pairs, int32_t *n_pairs_out);
 
+/* Move n sequences (host array seq_ids, distinct) from pool src to pool dst, all or nothing:
+ * the preemption and recovery of slide 15 (the newest request leaves at once and comes back
+ * by swap), with src and dst the device pool and a host pool, either way round.
+ *  - Every distinct block the sequences map gets one dst block, in first-use order (sequence
+ *    order, then logical order); its dst count is the number of moved sequences mapping it,
+ *    so sharing among them (forks, slide 14) survives the move.
+ *  - The sequences then leave src as pkv_seq_free would, in the order given: a block that a
+ *    sequence left behind still maps is copied but stays in src.
+ *  - pairs_out (host, int32[2*max_pairs]) receives the (src block, dst block) pairs, their
+ *    count in *n_pairs_out; the caller copies them (pkv_swap_blocks) before dst writes the
+ *    sequences' next tokens or src hands the freed blocks out again (same stream).
+ * PKV_ENOSEQ: a sequence not in src; PKV_EEXIST: a sequence already in dst; PKV_ENOMEM: dst
+ * has fewer free blocks than needed; PKV_EINVAL: duplicates, more pairs than max_pairs,
+ * different block sizes, or src == dst. On any error nothing changes. */
+int pkv_seq_migrate(pkv_pool *src, pkv_pool *dst, const int64_t *seq_ids, int32_t n, int32_t *pairs_out,
+                    int32_t max_pairs, int32_t *n_pairs_out);
+
 /* Block tables of n sequences as a dense host array tables_out[n][max_blocks] (row i for
  * seq_ids[i]), padded with pad_value past each sequence's blocks, and their lengths in
  * ctx_out[n] (host). A sequence with more than max_blocks blocks: PKV_EINVAL.

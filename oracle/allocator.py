@@ -122,6 +122,47 @@ class BlockPool:
             raise
         return slots, pairs
 
+    def migrate_to(self, dst, sids):
+        """Move whole sequences to another pool (preemption by swap, and its recovery: slide 15 of
+        the "vLLM and PagedAttention" deck -- a request leaves all at once and comes back by
+        swap). Returns the (block here, block in dst) pairs whose contents must be copied.
+
+        Readings (the pages say only "swap"): each distinct block the moving sequences map is
+        copied once, into a fresh dst block taken in first-use order (sequence order, then
+        logical order), so blocks they share stay shared in dst with the same number of
+        sharers; the sequences then leave this pool exactly as free_seq would, in the order
+        given, so a block another (unmoved) sequence still maps stays here. All or nothing: a
+        dst pool too short to take every block changes neither pool."""
+        if dst is self or dst.block_size != self.block_size:
+            raise ValueError("migrate needs two pools of one block size")
+        if len(set(sids)) != len(sids):
+            raise ValueError("a sequence appears twice")
+        for s in sids:
+            if s not in self.seqs:
+                raise KeyError(f"unknown sequence {s}")
+            if s in dst.seqs:
+                raise KeyError(f"sequence {s} exists in dst")
+        sharers = {}
+        first_use = []
+        for s in sids:
+            for b in self.seqs[s][0]:
+                if b not in sharers:
+                    sharers[b] = 0
+                    first_use.append(b)
+                sharers[b] += 1
+        if len(first_use) > dst.num_free():
+            raise OutOfBlocks()
+        moved_to = {}
+        for b in first_use:
+            nb = dst._take()
+            dst.ref[nb] = sharers[b]
+            moved_to[b] = nb
+        for s in sids:
+            blocks, n = self.seqs[s]
+            dst.seqs[s] = [[moved_to[b] for b in blocks], n]
+            self.free_seq(s)
+        return [(b, moved_to[b]) for b in first_use]
+
     def tables(self, sids, max_blocks, pad=-1):
         rows, ctx = [], []
         for s in sids:

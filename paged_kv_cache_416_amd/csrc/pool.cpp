@@ -229,4 +229,60 @@ int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t
     return PKV_OK;
 }
 
+// Moves whole sequences to another pool, all or nothing (slide 15: a preempted request leaves
+// at once and comes back by swap). Every distinct block the sequences map gets one block of
+// dst, in first-use order (sequence order, then logical order), carrying the sequences' own
+// reference counts; in src the sequences are then freed in the order given, as
+// pkv_seq_free would, so a block still mapped by a sequence left behind stays there.
+int pkv_seq_migrate(pkv_pool *src, pkv_pool *dst, const int64_t *seq_ids, int32_t n, int32_t *pairs_out,
+                    int32_t max_pairs, int32_t *n_pairs_out) {
+    if (n_pairs_out) *n_pairs_out = 0;
+    if (!src || !dst || src == dst || n < 0 || (n > 0 && !seq_ids) || max_pairs < 0 ||
+        (max_pairs > 0 && !pairs_out))
+        return fail(PKV_EINVAL, "pkv_seq_migrate: bad arguments");
+    if (src->block_size != dst->block_size)
+        return fail(PKV_EINVAL, "pkv_seq_migrate: block sizes differ (%d, %d)", src->block_size, dst->block_size);
+    std::unordered_set<int64_t> seen;
+    std::unordered_map<int32_t, int32_t> uses;  // src block -> references among the moved sequences
+    std::vector<int32_t> order;                 // distinct src blocks, first use first
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t id = seq_ids[i];
+        if (!seen.insert(id).second)
+            return fail(PKV_EINVAL, "pkv_seq_migrate: sequence %lld given twice", (long long)id);
+        auto it = src->seqs.find(id);
+        if (it == src->seqs.end())
+            return fail(PKV_ENOSEQ, "pkv_seq_migrate: unknown sequence %lld", (long long)id);
+        if (dst->seqs.count(id)) return fail(PKV_EEXIST, "pkv_seq_migrate: sequence %lld exists in dst", (long long)id);
+        for (int32_t b : it->second.blocks)
+            if (uses[b]++ == 0) order.push_back(b);
+    }
+    const int32_t need = static_cast<int32_t>(order.size());
+    if (need > max_pairs)
+        return fail(PKV_EINVAL, "pkv_seq_migrate: %d blocks to move, room for %d pairs", need, max_pairs);
+    if (need > static_cast<int32_t>(dst->free_stack.size()))
+        return fail(PKV_ENOMEM, "pkv_seq_migrate: %d blocks needed, %zu free", need, dst->free_stack.size());
+    std::unordered_map<int32_t, int32_t> to;
+    for (int32_t k = 0; k < need; ++k) {
+        const int32_t b = order[k], d = dst->take();
+        dst->ref[d] = uses[b];
+        to[b] = d;
+        pairs_out[2 * k] = b;
+        pairs_out[2 * k + 1] = d;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = src->seqs.find(seq_ids[i]);
+        pkv_pool::Seq moved;
+        moved.len = it->second.len;
+        moved.blocks.reserve(it->second.blocks.size());
+        for (int32_t b : it->second.blocks) {
+            moved.blocks.push_back(to[b]);
+            if (--src->ref[b] == 0) src->free_stack.push_back(b);
+        }
+        dst->seqs.emplace(seq_ids[i], std::move(moved));
+        src->seqs.erase(it);
+    }
+    if (n_pairs_out) *n_pairs_out = need;
+    return PKV_OK;
+}
+
 }  // extern "C"

@@ -105,3 +105,20 @@ class Pool:
         check(self._lib.pkv_build_block_tables(self._h, _i64p(ids), len(ids), max_blocks, pad, _i32p(tb),
                                                _i32p(ctx)))
         return tb, ctx
+
+    def migrate(self, dst: "Pool", sids):
+        """Move sequences sids to pool dst, all or nothing -> (src block, dst block) pairs int32 [P, 2]
+        to copy (preemption by swap and its recovery)."""
+        ids = np.ascontiguousarray(sids, dtype=np.int64)
+        max_pairs = sum(len(self.blocks(int(s))) for s in ids) if all(self._has(int(s)) for s in ids) else 0
+        pairs = np.zeros(2 * max(max_pairs, 1), np.int32)
+        npairs = ctypes.c_int32(0)
+        rc = self._lib.pkv_seq_migrate(self._h, dst._h, _i64p(ids), len(ids), _i32p(pairs), max_pairs,
+                                       ctypes.byref(npairs))
+        if rc == PKV_ENOMEM:
+            raise OutOfBlocks(rc, self._lib.pkv_last_error().decode())
+        check(rc)
+        return pairs[:2 * npairs.value].reshape(-1, 2)
+
+    def _has(self, sid: int) -> bool:
+        return self._lib.pkv_seq_len(self._h, sid) >= 0

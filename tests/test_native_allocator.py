@@ -140,3 +140,120 @@ def test_cow_pairs_native():
     assert len(pairs) == 3 and set(pairs[:, 0].tolist()) == {shared}
     assert p.ref_count(shared) == 1 and p.blocks(3)[-1] == shared
     assert p.ref_count(p.blocks(0)[0]) == 4
+
+
+class NativeVsModelTwoPools(RuleBasedStateMachine):
+    """A device pool and a host pool on both sides; sequences move between them (pkv_seq_migrate
+    against the model's migrate_to): identical pairs, blocks, lengths and reference counts."""
+
+    @initialize(nd=st.integers(1, 30), nh=st.integers(1, 30), B=st.sampled_from([1, 4, 16]),
+                seed=st.integers(0, 10**6))
+    def setup(self, nd, nh, B, seed):
+        rng = np.random.default_rng(seed)
+        od, oh = rng.permutation(nd), rng.permutation(nh)
+        self.native = {"dev": Pool(nd, B, od), "host": Pool(nh, B, oh)}
+        self.model = {"dev": BlockPool(nd, B, od), "host": BlockPool(nh, B, oh)}
+        self.where = {}
+        self.next = 0
+
+    def _ids(self, place):
+        return sorted(s for s, w in self.where.items() if w == place)
+
+    @rule()
+    def add(self):
+        self.native["dev"].add(self.next)
+        self.model["dev"].add(self.next)
+        self.where[self.next] = "dev"
+        self.next += 1
+
+    @precondition(lambda self: self.where)
+    @rule(data=st.data())
+    def fork(self, data):
+        p = data.draw(st.sampled_from(sorted(self.where)))
+        w = self.where[p]
+        self.native[w].fork(p, self.next)
+        self.model[w].fork(p, self.next)
+        self.where[self.next] = w
+        self.next += 1
+
+    @precondition(lambda self: self.where)
+    @rule(data=st.data())
+    def free(self, data):
+        s = data.draw(st.sampled_from(sorted(self.where)))
+        w = self.where.pop(s)
+        self.native[w].free(s)
+        self.model[w].free_seq(s)
+
+    @precondition(lambda self: any(w == "dev" for w in self.where.values()))
+    @rule(data=st.data())
+    def append(self, data):
+        sids = data.draw(st.lists(st.sampled_from(self._ids("dev")), min_size=1, max_size=3, unique=True))
+        reqs = [(s, data.draw(st.integers(0, 30))) for s in sids]
+        try:
+            m = self.model["dev"].append(reqs)
+        except ModelOOM:
+            m = None
+        try:
+            n = self.native["dev"].append(reqs)
+        except OutOfBlocks:
+            n = None
+        assert (m is None) == (n is None)
+
+    @precondition(lambda self: self.where)
+    @rule(data=st.data())
+    def move(self, data):
+        frm = data.draw(st.sampled_from(sorted(set(self.where.values()))))
+        to = "host" if frm == "dev" else "dev"
+        sids = data.draw(st.lists(st.sampled_from(self._ids(frm)), min_size=1, max_size=4, unique=True))
+        try:
+            m_pairs = self.model[frm].migrate_to(self.model[to], sids)
+        except ModelOOM:
+            m_pairs = None
+        try:
+            n_pairs = self.native[frm].migrate(self.native[to], sids)
+        except OutOfBlocks:
+            n_pairs = None
+        assert (m_pairs is None) == (n_pairs is None)
+        if m_pairs is not None:
+            assert [tuple(p) for p in n_pairs.tolist()] == m_pairs
+            for s in sids:
+                self.where[s] = to
+
+    @invariant()
+    def same_state(self):
+        if not hasattr(self, "native"):
+            return
+        for w in ("dev", "host"):
+            nat, mod = self.native[w], self.model[w]
+            assert nat.num_free() == mod.num_free()
+            for b in range(mod.num_blocks):
+                assert nat.ref_count(b) == mod.ref[b]
+            for s in self._ids(w):
+                assert nat.blocks(s) == mod.blocks(s) and nat.length(s) == mod.length(s)
+
+
+NativeVsModelTwoPools.TestCase.settings = settings(max_examples=120, stateful_step_count=40, deadline=None)
+TestNativeVsModelTwoPools = NativeVsModelTwoPools.TestCase
+
+
+def test_migrate_error_codes():
+    dev, host = Pool(6, 4), Pool(2, 4)
+    dev.add(1)
+    dev.append([(1, 9)])  # 3 blocks
+    with pytest.raises(OutOfBlocks):
+        dev.migrate(host, [1])
+    assert dev.blocks(1) and host.num_free() == 2  # nothing changed
+    with pytest.raises(PkvError) as e:
+        dev.migrate(host, [7])
+    assert e.value.code == _lib.PKV_ENOSEQ
+    with pytest.raises(PkvError) as e:
+        dev.migrate(dev, [1])
+    assert e.value.code == _lib.PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        dev.migrate(Pool(8, 8), [1])
+    assert e.value.code == _lib.PKV_EINVAL
+    big = Pool(8, 4)
+    big.add(1)
+    with pytest.raises(PkvError) as e:
+        dev.migrate(big, [1])
+    assert e.value.code == _lib.PKV_EEXIST

@@ -162,3 +162,137 @@ class PoolMachine(RuleBasedStateMachine):
 
 PoolMachine.TestCase.settings = settings(max_examples=120, stateful_step_count=40, deadline=None)
 TestPoolMachine = PoolMachine.TestCase
+
+
+class TwoPoolMachine(RuleBasedStateMachine):
+    """A device pool and a host pool (slide 15: a preempted request leaves by swap and comes
+    back): sequences move between them with migrate_to while add / fork / append / free go on.
+    Pins the move without restating it: both pools' invariants after every step, every
+    sequence still reads its own tokens through its table in the pool that holds it (block
+    contents carried by the returned pairs, as a block copy carries them), the moved
+    sequences map as many distinct blocks after the move as before (sharing kept), and a
+    move the destination cannot take changes neither pool."""
+
+    @initialize(nd=st.integers(1, 20), nh=st.integers(1, 20), B=st.sampled_from([1, 2, 4, 16]),
+                seed=st.integers(0, 1000))
+    def setup(self, nd, nh, B, seed):
+        rng = np.random.default_rng(seed)
+        self.pools = {"dev": BlockPool(nd, B, rng.permutation(nd)), "host": BlockPool(nh, B, rng.permutation(nh))}
+        self.where = {}  # sid -> "dev" | "host"
+        self.tokens = {}
+        self.owner = {"dev": {}, "host": {}}  # pool -> slot -> token id
+        self.next_id = 0
+
+    def _ids(self, place):
+        return sorted(s for s, w in self.where.items() if w == place)
+
+    @rule()
+    def add(self):
+        self.pools["dev"].add(self.next_id)
+        self.where[self.next_id] = "dev"
+        self.tokens[self.next_id] = []
+        self.next_id += 1
+
+    @precondition(lambda self: self.where)
+    @rule(data=st.data())
+    def fork(self, data):
+        p = data.draw(st.sampled_from(sorted(self.where)))
+        self.pools[self.where[p]].fork(p, self.next_id)
+        self.where[self.next_id] = self.where[p]
+        self.tokens[self.next_id] = list(self.tokens[p])
+        self.next_id += 1
+
+    @precondition(lambda self: self.where)
+    @rule(data=st.data())
+    def free(self, data):
+        s = data.draw(st.sampled_from(sorted(self.where)))
+        self.pools[self.where.pop(s)].free_seq(s)
+        del self.tokens[s]
+
+    @precondition(lambda self: any(w == "dev" for w in self.where.values()))
+    @rule(data=st.data())
+    def append(self, data):
+        pool = self.pools["dev"]
+        sids = data.draw(st.lists(st.sampled_from(self._ids("dev")), min_size=1, max_size=3, unique=True))
+        ns = [data.draw(st.integers(0, 9)) for _ in sids]
+        try:
+            slots, pairs = pool.append(list(zip(sids, ns)))
+        except OutOfBlocks:
+            return
+        B, own = pool.block_size, self.owner["dev"]
+        for src, dst in pairs:
+            for o in range(B):
+                if src * B + o in own:
+                    own[dst * B + o] = own[src * B + o]
+        i = 0
+        for sid, n in zip(sids, ns):
+            for _ in range(n):
+                tok = (sid, len(self.tokens[sid]))
+                self.tokens[sid].append(tok)
+                own[slots[i]] = tok
+                i += 1
+
+    def _move(self, data, frm, to):
+        sids = data.draw(st.lists(st.sampled_from(self._ids(frm)), min_size=1, max_size=4, unique=True))
+        src, dst = self.pools[frm], self.pools[to]
+        before = (list(src.free), list(src.ref), list(dst.free), list(dst.ref),
+                  {s: src.blocks(s) for s in src.seqs})
+        distinct = len({b for s in sids for b in src.blocks(s)})
+        try:
+            pairs = src.migrate_to(dst, sids)
+        except OutOfBlocks:
+            assert (list(src.free), list(src.ref), list(dst.free), list(dst.ref)) == before[:4]
+            assert {s: src.blocks(s) for s in src.seqs} == before[4]
+            assert distinct > dst.num_free()
+            return
+        assert len(pairs) == distinct == len({b for s in sids for b in dst.blocks(s)})
+        B = src.block_size
+        for a, b in pairs:  # the copy the caller runs
+            for o in range(B):
+                if a * B + o in self.owner[frm]:
+                    self.owner[to][b * B + o] = self.owner[frm][a * B + o]
+        for s in sids:
+            self.where[s] = to
+
+    @precondition(lambda self: any(w == "dev" for w in self.where.values()))
+    @rule(data=st.data())
+    def swap_out(self, data):
+        self._move(data, "dev", "host")
+
+    @precondition(lambda self: any(w == "host" for w in self.where.values()))
+    @rule(data=st.data())
+    def swap_in(self, data):
+        self._move(data, "host", "dev")
+
+    @invariant()
+    def both_pools_consistent_and_every_sequence_reads_its_tokens(self):
+        if not hasattr(self, "pools"):
+            return
+        for p in self.pools.values():
+            p.check_invariants()
+        for sid, toks in self.tokens.items():
+            place = self.where[sid]
+            pool, own = self.pools[place], self.owner[place]
+            assert sid in pool.seqs and all(sid not in q.seqs for n, q in self.pools.items() if n != place)
+            B = pool.block_size
+            blocks = pool.blocks(sid)
+            assert pool.length(sid) == len(toks)
+            for t, tok in enumerate(toks):
+                got = own.get(blocks[t // B] * B + t % B)
+                assert got is not None and got[1] == tok[1]
+
+
+TwoPoolMachine.TestCase.settings = settings(max_examples=120, stateful_step_count=40, deadline=None)
+TestTwoPoolMachine = TwoPoolMachine.TestCase
+
+
+def test_migrate_single_unshared_sequence_is_a_block_list_copy():
+    """A lone unshared sequence moves to the next free blocks of dst in LIFO order, one pair per
+    block in logical order, and its source blocks return to the free stack."""
+    src, dst = BlockPool(8, 4, [5, 1, 6, 0, 2, 3, 4, 7]), BlockPool(6, 4, [3, 0, 5, 1, 2, 4])
+    src.add(9)
+    src.append([(9, 10)])  # blocks 5, 1, 6
+    pairs = src.migrate_to(dst, [9])
+    assert pairs == [(5, 3), (1, 0), (6, 5)]
+    assert dst.blocks(9) == [3, 0, 5] and dst.length(9) == 10
+    assert src.num_free() == 8 and src.free[-3:] == [5, 1, 6]
