@@ -177,6 +177,24 @@ int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride
 int pkv_copy_blocks(void *const *k_caches, void *const *v_caches, int32_t num_layers, int64_t num_blocks,
                     int64_t block_bytes, const int32_t *pairs, int32_t num_pairs, hipStream_t stream);
 
+/* Copy whole blocks from one pool's caches to another's: for each pair p and cache c, block
+ * pairs[2p+1] of dst_caches[c] becomes a byte copy of block pairs[2p] of src_caches[c]. The
+ * copy half of preemption by swap (slide 15): with the pairs from pkv_seq_migrate, a device
+ * pool's caches to a host pool's (swap out) or back (swap in).
+ *  src_caches, dst_caches: host arrays of num_caches pointers (e.g. K and V of every layer),
+ *    each device memory or pinned host memory (allocated pinned through the HIP runtime; the
+ *    GPU reads or writes it over the host link), holding src_num_blocks / dst_num_blocks
+ *    blocks of block_bytes bytes; 16-byte aligned, block_bytes a multiple of 16.
+ *  pairs: host int32[2*num_pairs] (src block, dst block).
+ * One kernel launch per 8 caches and 224 pairs, on `stream`; pageable host memory is never
+ * touched by the device.
+ * PKV_EINVAL, with nothing launched: a block outside its pool, a destination block twice, a
+ * pointer that is neither device nor pinned host memory or whose allocation is smaller than
+ * its pool, a source overlapping its destination, bad sizes or alignment. */
+int pkv_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                    int64_t src_num_blocks, int64_t dst_num_blocks, int64_t block_bytes, const int32_t *pairs,
+                    int32_t num_pairs, hipStream_t stream);
+
 /* Bytes of fp32 workspace a split mode needs:
  *  partition_size > 0: num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4;
  *  PKV_PARTITION_BALANCED: W * (2 * num_q_heads * (head_dim + 2) * 4 + 8) + 4097 * 4, where W is

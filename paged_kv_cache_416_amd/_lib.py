@@ -43,6 +43,8 @@ SIGNATURES = {
     "pkv_reshape_and_cache": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32,
                                              _p]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i64, _i64, _pi32, _i32, _p]),
+    "pkv_swap_blocks": (ctypes.c_int, [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i64, _i64, _i64, _pi32, _i32,
+                                       _p]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                                   _i32, _f32, _i32, _p, _sz, _i32, _u32, _p]),

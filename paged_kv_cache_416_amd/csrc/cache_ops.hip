@@ -62,10 +62,127 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const CopyArgs a)
         *reinterpret_cast<u32x4 *>(dst + off) = *reinterpret_cast<const u32x4 *>(src + off);
 }
 
+constexpr int kSwapCaches = 8;
+constexpr int kSwapPairs = 224;
+constexpr int kSwapUnroll = 4;
+
+struct SwapArgs {
+    const char *src[kSwapCaches];
+    char *dst[kSwapCaches];
+    int32_t from[kSwapPairs];
+    int32_t to[kSwapPairs];
+    int64_t block_bytes;
+};
+
+// grid = (slices, pairs, caches): workgroup (x, p, c) copies slice x of pair p in cache c, from
+// one pool's cache to another's (either may be pinned host memory, reached over the host link:
+// kSwapUnroll independent 16-byte loads per thread keep the link's long round trips overlapped).
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(const SwapArgs a) {
+    const char *src = a.src[blockIdx.z] + a.from[blockIdx.y] * a.block_bytes;
+    char *dst = a.dst[blockIdx.z] + a.to[blockIdx.y] * a.block_bytes;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads * 16;
+    for (int64_t off = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 16; off < a.block_bytes;
+         off += step * kSwapUnroll) {
+        u32x4 x[kSwapUnroll];
+#pragma unroll
+        for (int u = 0; u < kSwapUnroll; ++u)
+            if (off + u * step < a.block_bytes) x[u] = *reinterpret_cast<const u32x4 *>(src + off + u * step);
+#pragma unroll
+        for (int u = 0; u < kSwapUnroll; ++u)
+            if (off + u * step < a.block_bytes) *reinterpret_cast<u32x4 *>(dst + off + u * step) = x[u];
+    }
+}
+
+// The device-usable address of `p` if it is device memory or host memory registered with the
+// runtime (pinned), with at least `bytes` of its allocation from p on; else an error code.
+int reachable(const char *fn, const void *p, int64_t bytes, const char *what, int c, void **dev) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PKV_EINVAL, "%s: %s[%d] is neither device memory nor pinned host memory", fn, what, c);
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeHost && attr.type != hipMemoryTypeManaged)
+        return fail(PKV_EINVAL, "%s: %s[%d] is neither device memory nor pinned host memory", fn, what, c);
+    *dev = attr.type == hipMemoryTypeHost && attr.devicePointer ? attr.devicePointer : const_cast<void *>(p);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) == hipSuccess) {
+        const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+        if (q < b || q - b + static_cast<uint64_t>(bytes) > size)
+            return fail(PKV_EINVAL, "%s: %s[%d] holds %zu bytes from its address, the pool needs %lld", fn, what, c,
+                        size - static_cast<size_t>(q - b), static_cast<long long>(bytes));
+    } else {
+        (void)hipGetLastError();
+    }
+    return PKV_OK;
+}
+
 }  // namespace
 }  // namespace pkv
 
 using namespace pkv;
+
+extern "C" int pkv_swap_blocks(const void *const *src_caches, void *const *dst_caches, int32_t num_caches,
+                               int64_t src_num_blocks, int64_t dst_num_blocks, int64_t block_bytes,
+                               const int32_t *pairs, int32_t num_pairs, hipStream_t stream) {
+    const char *fn = "pkv_swap_blocks";
+    if (num_caches < 0 || num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || block_bytes <= 0)
+        return fail(PKV_EINVAL, "%s: bad sizes", fn);
+    if (num_pairs == 0 || num_caches == 0) return PKV_OK;
+    if (!src_caches || !dst_caches || !pairs) return fail(PKV_EINVAL, "%s: NULL pointer", fn);
+    if (block_bytes % 16) return fail(PKV_EINVAL, "%s: block_bytes must be a multiple of 16", fn);
+    if (src_num_blocks > INT32_MAX || dst_num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: pool too large", fn);
+    {
+        std::vector<char> is_dst(dst_num_blocks, 0);
+        for (int32_t p = 0; p < num_pairs; ++p) {
+            const int32_t s = pairs[2 * p], d = pairs[2 * p + 1];
+            if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
+                return fail(PKV_EINVAL, "%s: pair %d (%d, %d) outside the pools (%lld, %lld blocks)", fn, p, s, d,
+                            (long long)src_num_blocks, (long long)dst_num_blocks);
+            if (is_dst[d]) return fail(PKV_EINVAL, "%s: block %d is a destination twice", fn, d);
+            is_dst[d] = 1;
+        }
+    }
+    std::vector<const char *> src(num_caches);
+    std::vector<char *> dst(num_caches);
+    for (int32_t c = 0; c < num_caches; ++c) {
+        if (!src_caches[c] || !dst_caches[c] || !aligned16(src_caches[c]) || !aligned16(dst_caches[c]))
+            return fail(PKV_EINVAL, "%s: cache %d pointer NULL or not 16-byte aligned", fn, c);
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src_caches[c]), d0 = reinterpret_cast<uintptr_t>(dst_caches[c]);
+        const uint64_t sb = static_cast<uint64_t>(src_num_blocks * block_bytes), db = static_cast<uint64_t>(dst_num_blocks * block_bytes);
+        if (s0 < d0 + db && d0 < s0 + sb)
+            return fail(PKV_EINVAL, "%s: cache %d's source and destination overlap (use pkv_copy_blocks)", fn, c);
+        void *ps = nullptr, *pd = nullptr;
+        int rc = reachable(fn, src_caches[c], src_num_blocks * block_bytes, "src_caches", c, &ps);
+        if (rc) return rc;
+        rc = reachable(fn, dst_caches[c], dst_num_blocks * block_bytes, "dst_caches", c, &pd);
+        if (rc) return rc;
+        src[c] = static_cast<const char *>(ps);
+        dst[c] = static_cast<char *>(pd);
+    }
+    const int64_t per_wg = static_cast<int64_t>(kThreads) * 16 * kSwapUnroll;  // 16 KiB per workgroup step
+    const unsigned slices = static_cast<unsigned>(std::min<int64_t>(ceil_div(block_bytes, per_wg), 64));
+    for (int32_t c0 = 0; c0 < num_caches; c0 += kSwapCaches) {
+        const int32_t nc = std::min(kSwapCaches, num_caches - c0);
+        for (int32_t p0 = 0; p0 < num_pairs; p0 += kSwapPairs) {
+            const int32_t np = std::min(kSwapPairs, num_pairs - p0);
+            SwapArgs a{};
+            for (int32_t c = 0; c < nc; ++c) {
+                a.src[c] = src[c0 + c];
+                a.dst[c] = dst[c0 + c];
+            }
+            for (int32_t p = 0; p < np; ++p) {
+                a.from[p] = pairs[2 * (p0 + p)];
+                a.to[p] = pairs[2 * (p0 + p) + 1];
+            }
+            a.block_bytes = block_bytes;
+            hipLaunchKernelGGL(swap_blocks_kernel, dim3(slices, np, nc), dim3(kThreads), 0, stream, a);
+            int rc = hip_status(hipGetLastError(), "pkv_swap_blocks launch");
+            if (rc) return rc;
+        }
+    }
+    return PKV_OK;
+}
 
 extern "C" int pkv_reshape_and_cache(const void *key, const void *value, int64_t key_stride, int64_t value_stride,
                                      void *k_cache, void *v_cache, int64_t num_blocks, const int64_t *slot_mapping,

@@ -75,6 +75,28 @@ def copy_blocks(k_caches, v_caches, pairs):
                                  pairs.shape[0], _stream()))
 
 
+def swap_blocks(src_caches, dst_caches, pairs):
+    """Copy blocks between two pools' caches (swap out / swap in). src_caches, dst_caches: lists of
+    contiguous tensors [N_src, ...] / [N_dst, ...] of one block shape, each on the device or in
+    pinned host memory; pairs: host (src block, dst block) pairs, e.g. from Pool.migrate."""
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    if pairs.shape[0] == 0:
+        return
+    C = len(src_caches)
+    if len(dst_caches) != C or C == 0:
+        raise ValueError("need one destination cache per source cache")
+    for t in list(src_caches) + list(dst_caches):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("caches must be device tensors or pinned host tensors")
+        if not t.is_contiguous() or t.shape[1:] != src_caches[0].shape[1:] or t.dtype != src_caches[0].dtype:
+            raise ValueError("caches must be contiguous, of one block shape and dtype")
+    bb = src_caches[0][0].numel() * src_caches[0].element_size()
+    sp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in src_caches])
+    dp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in dst_caches])
+    check(load().pkv_swap_blocks(sp, dp, C, src_caches[0].shape[0], dst_caches[0].shape[0], bb,
+                                 pairs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), pairs.shape[0], _stream()))
+
+
 def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
     return int(load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size))
 

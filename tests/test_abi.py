@@ -160,3 +160,25 @@ def test_read_probe_rejects_bad_arguments():
 def test_balanced_split_refuses_more_than_4096_sequences():
     assert _attn(S=4097, P=-1) == _lib.PKV_EUNSUPPORTED
     assert "4096" in _lib.load().pkv_last_error().decode()
+
+
+def test_swap_blocks_host_validation():
+    lib = _lib.load()
+    caches = (ctypes.c_void_p * 2)(FAKE, ctypes.c_void_p((1 << 30)))
+
+    def call(pairs, bb=4096, ns=8, nd=4, src=caches, dst=None):
+        pr = np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1))
+        d = dst if dst is not None else (ctypes.c_void_p * 2)(ctypes.c_void_p(1 << 31), ctypes.c_void_p(3 << 30))
+        return lib.pkv_swap_blocks(src, d, 2, ns, nd, bb, pr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   len(pr) // 2, NULL)
+
+    assert call([0, 4]) == _lib.PKV_EINVAL             # destination outside its pool
+    assert call([8, 0]) == _lib.PKV_EINVAL             # source outside its pool
+    assert call([0, 1, 2, 1]) == _lib.PKV_EINVAL       # a destination twice
+    assert call([0, 1], bb=4100) == _lib.PKV_EINVAL    # block bytes not a multiple of 16
+    assert call(np.zeros((0, 2))) == _lib.PKV_OK
+    same = (ctypes.c_void_p * 2)(FAKE, ctypes.c_void_p(1 << 30))
+    assert call([0, 1], src=same, dst=same) == _lib.PKV_EINVAL  # source overlaps destination
+    # fake addresses are neither device nor pinned host memory: refused before any launch
+    assert call([0, 1]) == _lib.PKV_EINVAL
+    assert b"pinned" in lib.pkv_last_error()
