@@ -90,6 +90,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
@@ -306,10 +307,62 @@ def main():
     if not args.no_contiguous:
         result["contiguous"] = contiguous_leg(w, P, args, dev, dt, attn_us, flags)
 
+    if args.swap:
+        result["swap"] = swap_leg(cache, w, dev, dt)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.workload, P, unique_b, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def swap_leg(cache, w, dev, dt, reps=5):
+    """Preemption by swap at this shape: the newest third of the batch moves to a pinned host pool
+    (pkv_seq_migrate + pkv_swap_blocks) and back, `reps` round trips; GB/s of block bytes moved
+    each way, next to the runtime's own pinned-host copies of the same byte count."""
+    import torch
+
+    from paged_kv_cache_416_amd import Pool, kernels
+    victims = list(w.batch[-max(1, len(w.batch) // 3):])
+    nblk = len({b for s in victims for b in cache.pool.blocks(s)})
+    host = Pool(nblk, w.block_size)
+    shape = (nblk,) + tuple(cache.k.shape[1:])
+    hk = torch.empty(shape, dtype=dt).pin_memory()
+    hv = torch.empty(shape, dtype=dt).pin_memory()
+    stream = torch.cuda.current_stream()
+    block_bytes = cache.k[0].numel() * cache.k.element_size()
+    t_out, t_in = [], []
+    for _ in range(reps):
+        for src_pool, dst_pool, src, dst, acc in ((cache.pool, host, [cache.k, cache.v], [hk, hv], t_out),
+                                                  (host, cache.pool, [hk, hv], [cache.k, cache.v], t_in)):
+            pairs = src_pool.migrate(dst_pool, victims)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kernels.swap_blocks(src, dst, pairs)
+            b.record(stream)
+            torch.cuda.synchronize()
+            acc.append(1e3 * a.elapsed_time(b))
+    nbytes = 2 * nblk * block_bytes
+    flat_h = torch.empty(nbytes // 2, dtype=torch.int16).pin_memory()
+    flat_d = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+
+    def copy_us(dst_t, src_t):
+        dst_t.copy_(src_t, non_blocking=True)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            dst_t.copy_(src_t, non_blocking=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / reps
+
+    d2h, h2d = copy_us(flat_h, flat_d), copy_us(flat_d, flat_h)
+    out_us, in_us = sorted(t_out)[len(t_out) // 2], sorted(t_in)[len(t_in) // 2]
+    return {"sequences": len(victims), "blocks": nblk, "bytes": nbytes,
+            "out_us": round(out_us, 1), "out_GB/s": round(nbytes / out_us / 1e3, 1),
+            "in_us": round(in_us, 1), "in_GB/s": round(nbytes / in_us / 1e3, 1),
+            "runtime_copy_GB/s": {"device_to_host": round(nbytes / d2h / 1e3, 1),
+                                  "host_to_device": round(nbytes / h2d / 1e3, 1)}}
 
 
 def read_probe_leg(nbytes, args, dev):
