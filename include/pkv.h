@@ -121,6 +121,36 @@ int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32
 int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_tokens, int32_t n_seqs,
                    int64_t *slots_out, int32_t *cow_pairs_out, int32_t max_pairs, int32_t *n_pairs_out);
 
+/* Prefix cache (the lesson note, section 3.1: hundreds of requests share one system prompt; a
+ * cryptographic hash of each prompt block finds existing blocks, which the new request maps,
+ * incrementing their counts, so their keys and values are not computed again).
+ * Digest of full prompt block j: SHA-256 of (digest of block j-1, or 32 zero bytes for j = 0)
+ * followed by the block's block_size token ids as little-endian int32: equal digests mean
+ * equal prefixes. Only full prompt blocks are hashed. A hashed block that falls free keeps its
+ * digest and contents: free blocks without a digest are handed out first (the usual LIFO
+ * order), then hashed free blocks, least recently freed first, each losing its digest. A
+ * digest names one block: a new prompt block whose digest another block holds (a later block
+ * of a chain whose earlier block was evicted) takes the digest over, and the other block
+ * becomes an ordinary one (on the LIFO stack if free). */
+
+/* Chained digests of the full blocks of tokens[n_tokens] into digests_out[32 * k], k =
+ * n_tokens / block_size full blocks (returned); PKV_EINVAL if k > max_blocks. Host only. */
+int pkv_prompt_digests(const int32_t *tokens, int64_t n_tokens, int32_t block_size, uint8_t *digests_out,
+                       int64_t max_blocks);
+
+/* Add sequence seq_id with a prompt of n_tokens token ids (host arrays). Its leading full
+ * blocks whose digests the pool holds are mapped and counted (a hit on a free hashed block
+ * takes it back from the free list); the rest get blocks as pkv_seq_append would, each new
+ * full block registered under its digest. slots_out (host, int64[n_tokens]) receives -1 for
+ * the n_cached_out leading tokens whose keys and values are already in the cache (a negative
+ * slot is skipped by pkv_reshape_and_cache) and the slot of every other token.
+ * PKV_EEXIST: seq_id exists; PKV_ENOMEM: not enough free blocks (nothing changes). */
+int pkv_seq_add_prompt(pkv_pool *pool, int64_t seq_id, const int32_t *tokens, int32_t n_tokens, int64_t *slots_out,
+                       int32_t *n_cached_out);
+
+/* Blocks the pool holds a digest for (in use or free). */
+int32_t pkv_pool_num_cached(const pkv_pool *pool);
+
 /* Move n sequences (host array seq_ids, distinct) from pool src to pool dst, all or nothing:
  * the preemption and recovery of slide 15 (the newest request leaves at once and comes back
  * by swap), with src and dst the device pool and a host pool, either way round.

@@ -21,10 +21,36 @@ same choices independently):
     the next one handed out;
   * within one batched append, sequences are served in the order given, and
     the whole batch fails, changing nothing, if the pool runs short.
+
+Prefix cache (lesson note section 3.1: a cryptographic hash of each prompt block;
+a new request whose block hashes to an existing block maps it and increments its
+count). Readings: the digest of full prompt block j is SHA-256 (Python's hashlib)
+of the previous block's digest (32 zero bytes for the first) followed by the
+block's token ids as little-endian int32, so equal digests mean equal prefixes;
+only full prompt blocks are hashed and hits are taken as a prefix of the prompt; a
+hashed block that falls free keeps its digest until the pool needs it -- free
+blocks without a digest are handed out first (the LIFO stack above), then hashed
+free blocks, least recently freed first, each losing its digest. A digest is held by one
+block: when a new prompt block's digest is already held (a later block of a chain whose
+earlier block was evicted), the new block takes it over and the old block becomes an
+ordinary block, joining the LIFO stack if it is free.
 """
 from __future__ import annotations
 
 import copy
+import hashlib
+
+import numpy as np
+
+
+def prompt_digests(tokens, block_size):
+    """Chained digests of the full blocks of a token stream (lesson note section 3.1)."""
+    out, prev = [], bytes(32)
+    for j in range(len(tokens) // block_size):
+        block = np.asarray(tokens[j * block_size:(j + 1) * block_size], dtype="<i4").tobytes()
+        prev = hashlib.sha256(prev + block).digest()
+        out.append(prev)
+    return out
 
 
 class OutOfBlocks(Exception):
@@ -41,12 +67,18 @@ class BlockPool:
         self.num_blocks = num_blocks
         self.block_size = block_size
         self.free = order[::-1]  # top of the stack is the end of the list
+        self.cached_free = []  # free blocks that keep a digest, least recently freed first
+        self.digest_of = {}  # block -> digest
+        self.block_of = {}  # digest -> block
         self.ref = [0] * num_blocks
         self.seqs = {}  # sid -> [blocks(list), length(int)]
 
     # -- queries ---------------------------------------------------------
     def num_free(self):
-        return len(self.free)
+        return len(self.free) + len(self.cached_free)
+
+    def num_cached(self):
+        return len(self.block_of)
 
     def length(self, sid):
         return self.seqs[sid][1]
@@ -73,12 +105,64 @@ class BlockPool:
         for b in blocks:
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                self.free.append(b)
+                self._release(b)
+
+    def _release(self, b):
+        if b in self.digest_of:
+            self.cached_free.append(b)
+        else:
+            self.free.append(b)
 
     def _take(self):
-        b = self.free.pop()
+        if self.free:
+            b = self.free.pop()
+        else:
+            b = self.cached_free.pop(0)
+            del self.block_of[self.digest_of.pop(b)]
         self.ref[b] = 1
         return b
+
+    def add_prompt(self, sid, tokens):
+        """New sequence with a prompt (prefix cache). Returns (slots, n_cached): -1 for the leading
+        tokens whose blocks were found by digest, the slot of every other token."""
+        if sid in self.seqs:
+            raise KeyError(f"sequence {sid} exists")
+        B = self.block_size
+        digests = prompt_digests(tokens, B)
+        hits = []
+        for d in digests:
+            if d not in self.block_of:
+                break
+            hits.append(self.block_of[d])
+        revive = sum(1 for b in hits if self.ref[b] == 0)
+        fresh = len(digests) - len(hits) + (1 if len(tokens) % B else 0)
+        if revive + fresh > self.num_free():
+            raise OutOfBlocks()
+        blocks = []
+        for b in hits:
+            if self.ref[b] == 0:
+                self.cached_free.remove(b)
+            self.ref[b] += 1
+            blocks.append(b)
+        for d in digests[len(hits):]:
+            b = self._take()
+            old = self.block_of.get(d)
+            if old is not None:
+                # a later block of a chain whose earlier block was evicted: the new block takes
+                # the digest over and the old one becomes an ordinary block (free, if unused)
+                del self.digest_of[old]
+                if self.ref[old] == 0:
+                    self.cached_free.remove(old)
+                    self.free.append(old)
+            self.digest_of[b] = d
+            self.block_of[d] = b
+            blocks.append(b)
+        if len(tokens) % B:
+            blocks.append(self._take())
+        self.seqs[sid] = [blocks, len(tokens)]
+        n_cached = len(hits) * B
+        slots = [-1 if t < n_cached else blocks[t // B] * B + t % B for t in range(len(tokens))]
+        return slots, n_cached
 
     def _append_one(self, sid, n):
         B = self.block_size
@@ -87,7 +171,7 @@ class BlockPool:
         if n == 0:
             return [], pairs
         if length % B and self.ref[blocks[-1]] > 1:
-            if not self.free:
+            if self.num_free() == 0:
                 raise OutOfBlocks()
             old = blocks[-1]
             new = self._take()
@@ -95,7 +179,7 @@ class BlockPool:
             blocks[-1] = new
             pairs.append((old, new))
         while len(blocks) * B < length + n:
-            if not self.free:
+            if self.num_free() == 0:
                 raise OutOfBlocks()
             blocks.append(self._take())
         slots = [blocks[t // B] * B + t % B for t in range(length, length + n)]
@@ -110,7 +194,8 @@ class BlockPool:
         for s in sids:
             if s not in self.seqs:
                 raise KeyError(f"unknown sequence {s}")
-        saved = (list(self.free), list(self.ref), copy.deepcopy(self.seqs))
+        saved = (list(self.free), list(self.ref), copy.deepcopy(self.seqs), list(self.cached_free),
+                 dict(self.digest_of), dict(self.block_of))
         slots, pairs = [], []
         try:
             for sid, n in requests:
@@ -118,7 +203,7 @@ class BlockPool:
                 slots += sl
                 pairs += pr
         except OutOfBlocks:
-            self.free, self.ref, self.seqs = saved
+            self.free, self.ref, self.seqs, self.cached_free, self.digest_of, self.block_of = saved
             raise
         return slots, pairs
 
@@ -174,15 +259,19 @@ class BlockPool:
         return rows, ctx
 
     def check_invariants(self):
-        """One pool; reference counts count sharers; a block is free iff its count is zero."""
+        """One pool; reference counts count sharers; a block is free iff its count is zero; the
+        digest index and the hashed free blocks agree."""
         N = self.num_blocks
-        assert len(set(self.free)) == len(self.free)
+        free = self.free + self.cached_free
+        assert len(set(free)) == len(free)
         used = {b for blocks, _ in self.seqs.values() for b in blocks}
-        assert len(self.free) + len(used) == N
+        assert len(free) + len(used) == N
         for b in range(N):
             holders = sum(blocks.count(b) for blocks, _ in self.seqs.values())
             assert self.ref[b] == holders, (b, self.ref[b], holders)
-            assert (b in self.free) == (holders == 0)
+            assert (b in free) == (holders == 0)
+        assert all(b in self.digest_of for b in self.cached_free) and not set(self.free) & set(self.digest_of)
+        assert {d: b for b, d in self.digest_of.items()} == self.block_of
         B = self.block_size
         for blocks, n in self.seqs.values():
             assert len(blocks) == -(-n // B)

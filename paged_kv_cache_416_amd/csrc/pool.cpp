@@ -11,6 +11,20 @@
 // is handed out first; a freed block is the next one handed out); a freed
 // sequence returns its blocks in logical order; a batched append serves its
 // sequences in the order given.
+//
+// Prefix cache (the lesson note, section 3.1: a cryptographic hash of each prompt block; a new
+// request whose prompt block hashes to an existing block maps that block and increments its
+// count). Readings: the digest of full prompt block j is SHA-256 of (the digest of block j-1,
+// or 32 zero bytes for j = 0) followed by the block's token ids as little-endian int32, so equal
+// digests mean equal prefixes, which is what a block's keys and values depend on; only full
+// prompt blocks are hashed, and hits are taken as a prefix of the prompt. A hashed block that
+// falls free keeps its digest and contents until the pool needs it: free blocks without a
+// digest are handed out first (the LIFO stack), then hashed free blocks, least recently freed
+// first, each dropping its digest.
+#include <array>
+#include <cstring>
+#include <iterator>
+#include <list>
 #include <unordered_map>
 #include <unordered_set>
 #include <vector>
@@ -19,6 +33,36 @@
 
 using pkv::fail;
 
+namespace pkv {
+void sha256(const uint8_t *data, size_t n, uint8_t out[32]);
+}
+
+namespace {
+typedef std::array<uint8_t, 32> Digest;
+struct DigestHash {
+    size_t operator()(const Digest &d) const {
+        size_t h;
+        std::memcpy(&h, d.data(), sizeof h);
+        return h;
+    }
+};
+
+// Chained digests of the full blocks of a token stream (see above).
+void prompt_digests(const int32_t *tokens, int64_t n_full, int32_t block_size, Digest *out) {
+    std::vector<uint8_t> buf(32 + static_cast<size_t>(block_size) * 4);
+    Digest prev{};
+    for (int64_t j = 0; j < n_full; ++j) {
+        std::memcpy(buf.data(), prev.data(), 32);
+        for (int32_t t = 0; t < block_size; ++t) {
+            const uint32_t v = static_cast<uint32_t>(tokens[j * block_size + t]);
+            for (int b = 0; b < 4; ++b) buf[32 + 4 * t + b] = static_cast<uint8_t>(v >> (8 * b));
+        }
+        pkv::sha256(buf.data(), buf.size(), out[j].data());
+        prev = out[j];
+    }
+}
+}  // namespace
+
 struct pkv_pool {
     struct Seq {
         std::vector<int32_t> blocks;  // logical block j -> physical block
@@ -26,15 +70,40 @@ struct pkv_pool {
     };
     int32_t num_blocks = 0;
     int32_t block_size = 0;
-    std::vector<int32_t> free_stack;  // back() is handed out next
-    std::vector<int32_t> ref;         // sequences mapping each block
+    std::vector<int32_t> free_stack;  // free blocks without a digest; back() is handed out next
+    std::list<int32_t> cached_free;   // free blocks that keep a digest, least recently freed first
+    std::vector<std::list<int32_t>::iterator> lru_pos;
+    std::vector<int32_t> ref;  // sequences mapping each block
+    std::vector<Digest> digest;
+    std::vector<char> has_digest;
+    std::unordered_map<Digest, int32_t, DigestHash> by_digest;
     std::unordered_map<int64_t, Seq> seqs;
 
+    int64_t available() const { return static_cast<int64_t>(free_stack.size() + cached_free.size()); }
+
     int32_t take() {
-        int32_t b = free_stack.back();
-        free_stack.pop_back();
+        int32_t b;
+        if (!free_stack.empty()) {
+            b = free_stack.back();
+            free_stack.pop_back();
+        } else {  // evict the least recently freed hashed block
+            b = cached_free.front();
+            cached_free.pop_front();
+            by_digest.erase(digest[b]);
+            has_digest[b] = 0;
+        }
         ref[b] = 1;
         return b;
+    }
+
+    // b's count just reached zero
+    void release(int32_t b) {
+        if (has_digest[b]) {
+            cached_free.push_back(b);
+            lru_pos[b] = std::prev(cached_free.end());
+        } else {
+            free_stack.push_back(b);
+        }
     }
 };
 
@@ -50,6 +119,9 @@ int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_
     p->num_blocks = num_blocks;
     p->block_size = block_size;
     p->ref.assign(num_blocks, 0);
+    p->digest.resize(num_blocks);
+    p->has_digest.assign(num_blocks, 0);
+    p->lru_pos.resize(num_blocks);
     p->free_stack.resize(num_blocks);
     if (free_order) {
         std::vector<char> seen(num_blocks, 0);
@@ -74,7 +146,11 @@ void pkv_pool_destroy(pkv_pool *pool) { delete pool; }
 int32_t pkv_pool_num_blocks(const pkv_pool *pool) { return pool ? pool->num_blocks : PKV_EINVAL; }
 int32_t pkv_pool_block_size(const pkv_pool *pool) { return pool ? pool->block_size : PKV_EINVAL; }
 int32_t pkv_pool_num_free(const pkv_pool *pool) {
-    return pool ? static_cast<int32_t>(pool->free_stack.size()) : PKV_EINVAL;
+    return pool ? static_cast<int32_t>(pool->available()) : PKV_EINVAL;
+}
+
+int32_t pkv_pool_num_cached(const pkv_pool *pool) {
+    return pool ? static_cast<int32_t>(pool->by_digest.size()) : PKV_EINVAL;
 }
 
 int32_t pkv_block_ref_count(const pkv_pool *pool, int32_t block) {
@@ -94,7 +170,7 @@ int pkv_seq_free(pkv_pool *pool, int64_t seq_id) {
     auto it = pool->seqs.find(seq_id);
     if (it == pool->seqs.end()) return fail(PKV_ENOSEQ, "pkv_seq_free: unknown sequence %lld", (long long)seq_id);
     for (int32_t b : it->second.blocks)
-        if (--pool->ref[b] == 0) pool->free_stack.push_back(b);
+        if (--pool->ref[b] == 0) pool->release(b);
     pool->seqs.erase(it);
     return PKV_OK;
 }
@@ -177,9 +253,9 @@ int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_toke
     if (total_tokens > 0 && !slots_out) return fail(PKV_EINVAL, "pkv_seq_append: slots_out is NULL");
     if (pairs > max_pairs)
         return fail(PKV_EINVAL, "pkv_seq_append: %d copy-on-write pairs, room for %d", pairs, max_pairs);
-    if (need > static_cast<int64_t>(pool->free_stack.size()))
-        return fail(PKV_ENOMEM, "pkv_seq_append: batch needs %lld blocks, %zu free", (long long)need,
-                    pool->free_stack.size());
+    if (need > pool->available())
+        return fail(PKV_ENOMEM, "pkv_seq_append: batch needs %lld blocks, %lld free", (long long)need,
+                    (long long)pool->available());
     // Apply.
     int64_t k = 0;
     int32_t np = 0;
@@ -229,6 +305,80 @@ int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t
     return PKV_OK;
 }
 
+int pkv_prompt_digests(const int32_t *tokens, int64_t n_tokens, int32_t block_size, uint8_t *digests_out,
+                       int64_t max_blocks) {
+    if (n_tokens < 0 || block_size <= 0 || (n_tokens > 0 && !tokens) || max_blocks < 0)
+        return fail(PKV_EINVAL, "pkv_prompt_digests: bad arguments");
+    const int64_t n_full = n_tokens / block_size;
+    if (n_full > max_blocks || (n_full > 0 && !digests_out))
+        return fail(PKV_EINVAL, "pkv_prompt_digests: %lld full blocks, room for %lld", (long long)n_full,
+                    (long long)max_blocks);
+    if (n_full > INT32_MAX) return fail(PKV_EINVAL, "pkv_prompt_digests: too many blocks");
+    std::vector<Digest> d(n_full);
+    prompt_digests(tokens, n_full, block_size, d.data());
+    for (int64_t j = 0; j < n_full; ++j) std::memcpy(digests_out + 32 * j, d[j].data(), 32);
+    return static_cast<int32_t>(n_full);
+}
+
+int pkv_seq_add_prompt(pkv_pool *pool, int64_t seq_id, const int32_t *tokens, int32_t n_tokens, int64_t *slots_out,
+                       int32_t *n_cached_out) {
+    if (n_cached_out) *n_cached_out = 0;
+    if (!pool || n_tokens < 0 || (n_tokens > 0 && (!tokens || !slots_out)))
+        return fail(PKV_EINVAL, "pkv_seq_add_prompt: bad arguments");
+    if (pool->seqs.count(seq_id))
+        return fail(PKV_EEXIST, "pkv_seq_add_prompt: sequence %lld exists", (long long)seq_id);
+    const int32_t B = pool->block_size;
+    const int32_t n_full = n_tokens / B;
+    std::vector<Digest> d(n_full);
+    prompt_digests(tokens, n_full, B, d.data());
+    // cached prefix: leading full blocks whose digests the pool holds
+    std::vector<int32_t> hit;
+    int64_t revive = 0;  // hits on free (cached) blocks: they leave the free lists
+    for (int32_t j = 0; j < n_full; ++j) {
+        auto f = pool->by_digest.find(d[j]);
+        if (f == pool->by_digest.end()) break;
+        hit.push_back(f->second);
+        if (pool->ref[f->second] == 0) ++revive;
+    }
+    const int32_t n_hit = static_cast<int32_t>(hit.size());
+    const int64_t fresh = (n_full - n_hit) + (n_tokens % B ? 1 : 0);
+    if (revive + fresh > pool->available())
+        return fail(PKV_ENOMEM, "pkv_seq_add_prompt: %lld blocks needed, %lld free", (long long)(revive + fresh),
+                    (long long)pool->available());
+    pkv_pool::Seq q;
+    q.len = n_tokens;
+    for (int32_t b : hit) {
+        if (pool->ref[b] == 0) pool->cached_free.erase(pool->lru_pos[b]);
+        ++pool->ref[b];
+        q.blocks.push_back(b);
+    }
+    for (int32_t j = n_hit; j < n_full; ++j) {
+        const int32_t b = pool->take();
+        auto f = pool->by_digest.find(d[j]);
+        if (f != pool->by_digest.end()) {
+            // a later block of a chain whose earlier block was evicted: the new block takes the
+            // digest over and the old one becomes an ordinary block (free, if unused)
+            const int32_t old = f->second;
+            pool->has_digest[old] = 0;
+            if (pool->ref[old] == 0) {
+                pool->cached_free.erase(pool->lru_pos[old]);
+                pool->free_stack.push_back(old);
+            }
+        }
+        pool->digest[b] = d[j];
+        pool->has_digest[b] = 1;
+        pool->by_digest[d[j]] = b;
+        q.blocks.push_back(b);
+    }
+    if (n_tokens % B) q.blocks.push_back(pool->take());
+    const int64_t cached = static_cast<int64_t>(n_hit) * B;
+    for (int64_t t = 0; t < n_tokens; ++t)
+        slots_out[t] = t < cached ? -1 : static_cast<int64_t>(q.blocks[t / B]) * B + t % B;
+    pool->seqs.emplace(seq_id, std::move(q));
+    if (n_cached_out) *n_cached_out = static_cast<int32_t>(cached);
+    return PKV_OK;
+}
+
 // Moves whole sequences to another pool, all or nothing (slide 15: a preempted request leaves
 // at once and comes back by swap). Every distinct block the sequences map gets one block of
 // dst, in first-use order (sequence order, then logical order), carrying the sequences' own
@@ -259,8 +409,8 @@ int pkv_seq_migrate(pkv_pool *src, pkv_pool *dst, const int64_t *seq_ids, int32_
     const int32_t need = static_cast<int32_t>(order.size());
     if (need > max_pairs)
         return fail(PKV_EINVAL, "pkv_seq_migrate: %d blocks to move, room for %d pairs", need, max_pairs);
-    if (need > static_cast<int32_t>(dst->free_stack.size()))
-        return fail(PKV_ENOMEM, "pkv_seq_migrate: %d blocks needed, %zu free", need, dst->free_stack.size());
+    if (need > dst->available())
+        return fail(PKV_ENOMEM, "pkv_seq_migrate: %d blocks needed, %lld free", need, (long long)dst->available());
     std::unordered_map<int32_t, int32_t> to;
     for (int32_t k = 0; k < need; ++k) {
         const int32_t b = order[k], d = dst->take();
@@ -276,7 +426,7 @@ int pkv_seq_migrate(pkv_pool *src, pkv_pool *dst, const int64_t *seq_ids, int32_
         moved.blocks.reserve(it->second.blocks.size());
         for (int32_t b : it->second.blocks) {
             moved.blocks.push_back(to[b]);
-            if (--src->ref[b] == 0) src->free_stack.push_back(b);
+            if (--src->ref[b] == 0) src->release(b);
         }
         dst->seqs.emplace(seq_ids[i], std::move(moved));
         src->seqs.erase(it);

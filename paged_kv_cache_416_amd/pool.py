@@ -122,3 +122,29 @@ class Pool:
 
     def _has(self, sid: int) -> bool:
         return self._lib.pkv_seq_len(self._h, sid) >= 0
+
+    def add_prompt(self, sid: int, tokens):
+        """Add sequence sid with prompt token ids (prefix cache) -> (slots int64 [n], n_cached):
+        slots of cached tokens are -1."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.zeros(max(len(toks), 1), np.int64)
+        n_cached = ctypes.c_int32(0)
+        rc = self._lib.pkv_seq_add_prompt(self._h, sid, _i32p(toks), len(toks), _i64p(slots), ctypes.byref(n_cached))
+        if rc == PKV_ENOMEM:
+            raise OutOfBlocks(rc, self._lib.pkv_last_error().decode())
+        check(rc)
+        return slots[:len(toks)], n_cached.value
+
+    def num_cached(self) -> int:
+        return self._lib.pkv_pool_num_cached(self._h)
+
+
+def prompt_digests(tokens, block_size):
+    """Chained SHA-256 digests of the full blocks of a token stream -> bytes array [k, 32]."""
+    toks = np.ascontiguousarray(tokens, dtype=np.int32)
+    k = len(toks) // block_size
+    out = np.zeros((max(k, 1), 32), np.uint8)
+    n = load().pkv_prompt_digests(_i32p(toks), len(toks), block_size,
+                                  out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), k)
+    check(0 if n >= 0 else n)
+    return out[:n]

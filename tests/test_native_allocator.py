@@ -257,3 +257,96 @@ def test_migrate_error_codes():
     with pytest.raises(PkvError) as e:
         dev.migrate(big, [1])
     assert e.value.code == _lib.PKV_EEXIST
+
+
+class NativeVsModelPrefix(RuleBasedStateMachine):
+    """Prefix cache: pkv_seq_add_prompt against the model's add_prompt, among appends, forks and
+    frees, with prompts from a few shared system prompts so hits, revivals and evictions all
+    happen: identical slots, cached counts, blocks and counts, and the native digests equal the
+    model's (hashlib)."""
+
+    @initialize(N=st.integers(2, 30), B=st.sampled_from([1, 2, 4, 16]), seed=st.integers(0, 10**6))
+    def setup(self, N, B, seed):
+        rng = np.random.default_rng(seed)
+        order = rng.permutation(N)
+        self.native, self.model = Pool(N, B, order), BlockPool(N, B, order)
+        self.systems = [rng.integers(0, 4, size=rng.integers(0, 3 * B + 2)).tolist() for _ in range(3)]
+        self.ids, self.next = [], 0
+
+    @rule(data=st.data())
+    def add_prompt(self, data):
+        prompt = data.draw(st.sampled_from(self.systems)) + data.draw(st.lists(st.integers(0, 4), max_size=2 * B_MAX))
+        try:
+            m = self.model.add_prompt(self.next, prompt)
+        except ModelOOM:
+            m = None
+        try:
+            n = self.native.add_prompt(self.next, prompt)
+        except OutOfBlocks:
+            n = None
+        assert (m is None) == (n is None)
+        if m is not None:
+            assert n[0].tolist() == m[0] and n[1] == m[1]
+            self.ids.append(self.next)
+        self.next += 1
+
+    @precondition(lambda self: self.ids)
+    @rule(data=st.data())
+    def free(self, data):
+        s = data.draw(st.sampled_from(self.ids))
+        self.native.free(s)
+        self.model.free_seq(s)
+        self.ids.remove(s)
+
+    @precondition(lambda self: self.ids)
+    @rule(data=st.data())
+    def fork(self, data):
+        s = data.draw(st.sampled_from(self.ids))
+        self.native.fork(s, self.next)
+        self.model.fork(s, self.next)
+        self.ids.append(self.next)
+        self.next += 1
+
+    @precondition(lambda self: self.ids)
+    @rule(data=st.data())
+    def append(self, data):
+        s = data.draw(st.sampled_from(self.ids))
+        n = data.draw(st.integers(1, 6))
+        try:
+            m = self.model.append([(s, n)])
+        except ModelOOM:
+            m = None
+        try:
+            nat = self.native.append([(s, n)])
+        except OutOfBlocks:
+            nat = None
+        assert (m is None) == (nat is None)
+        if m is not None:
+            assert nat[0].tolist() == m[0] and [tuple(p) for p in nat[1].tolist()] == m[1]
+
+    @invariant()
+    def same_state(self):
+        if not hasattr(self, "native"):
+            return
+        assert self.native.num_free() == self.model.num_free()
+        assert self.native.num_cached() == self.model.num_cached()
+        for b in range(self.model.num_blocks):
+            assert self.native.ref_count(b) == self.model.ref[b]
+        for s in self.ids:
+            assert self.native.blocks(s) == self.model.blocks(s) and self.native.length(s) == self.model.length(s)
+
+
+B_MAX = 16
+NativeVsModelPrefix.TestCase.settings = settings(max_examples=150, stateful_step_count=40, deadline=None)
+TestNativeVsModelPrefix = NativeVsModelPrefix.TestCase
+
+
+@pytest.mark.parametrize("B", [1, 7, 13, 16, 32])
+def test_native_digests_equal_hashlib_chain(B):
+    """The native SHA-256 (constants computed from their definition) against hashlib on chained
+    block digests; block sizes 7 and 13 put the padding on both sides of a 64-byte boundary."""
+    from oracle.allocator import prompt_digests as model_digests
+    from paged_kv_cache_416_amd.pool import prompt_digests
+    toks = np.random.default_rng(B).integers(-2**31, 2**31 - 1, size=6 * B + 1, dtype=np.int64).astype(np.int32)
+    got = prompt_digests(toks, B)
+    assert [bytes(r) for r in got] == model_digests(toks.tolist(), B)

@@ -296,3 +296,198 @@ def test_migrate_single_unshared_sequence_is_a_block_list_copy():
     assert pairs == [(5, 3), (1, 0), (6, 5)]
     assert dst.blocks(9) == [3, 0, 5] and dst.length(9) == 10
     assert src.num_free() == 8 and src.free[-3:] == [5, 1, 6]
+
+
+# ---------------------------------------------------------------- prefix cache (lesson note 3.1)
+
+from oracle.allocator import prompt_digests  # noqa: E402
+
+
+@pytest.mark.parametrize("B", [1, 7, 8, 16, 32])
+def test_digests_chain_over_the_prefix(B):
+    """Equal prompts give equal digests; changing one token of block j changes the digests of
+    blocks j.. and of no earlier block (a block's digest stands for its whole prefix)."""
+    rng = np.random.default_rng(B)
+    toks = rng.integers(0, 50000, size=5 * B + 3 % B).tolist()
+    d = prompt_digests(toks, B)
+    assert len(d) == 5 and len(set(d)) == 5 and all(len(x) == 32 for x in d)
+    assert prompt_digests(list(toks), B) == d
+    for j in range(5):
+        t2 = list(toks)
+        t2[j * B + B // 2] += 1
+        d2 = prompt_digests(t2, B)
+        assert d2[:j] == d[:j] and all(a != b for a, b in zip(d2[j:], d[j:]))
+    # the same block contents after a different prefix hash differently
+    assert prompt_digests(toks[B:2 * B], B)[0] != d[1]
+
+
+def test_shared_system_prompt_maps_the_same_blocks():
+    p = BlockPool(16, 4)
+    sys_prompt = [11, 12, 13, 14, 21, 22, 23, 24, 31, 32, 33, 34]
+    s1, c1 = p.add_prompt(1, sys_prompt + [7, 8])
+    assert c1 == 0 and -1 not in s1
+    s2, c2 = p.add_prompt(2, sys_prompt + [9])
+    assert c2 == 12 and s2[:12] == [-1] * 12 and s2[12] >= 0
+    assert p.blocks(2)[:3] == p.blocks(1)[:3] and p.blocks(2)[3] != p.blocks(1)[3]
+    assert [p.ref[b] for b in p.blocks(1)[:3]] == [2, 2, 2] and p.num_cached() == 3
+    # a prompt that leaves the system prompt inside block 1 shares block 0 only
+    s3, c3 = p.add_prompt(3, sys_prompt[:5] + [99] + sys_prompt[6:])
+    assert c3 == 4 and p.blocks(3)[0] == p.blocks(1)[0] and p.blocks(3)[1] != p.blocks(1)[1]
+    p.check_invariants()
+
+
+def test_freed_prompt_blocks_stay_cached_until_needed():
+    """Freed hashed blocks are found again; blocks without a digest are handed out before them,
+    and then the least recently freed hashed block goes first."""
+    p = BlockPool(6, 2)
+    p.add_prompt(1, [1, 2, 3, 4])   # hashed blocks a, b
+    p.add_prompt(2, [5, 6, 7])      # hashed c, partial d
+    a, b = p.blocks(1)
+    c, d = p.blocks(2)
+    p.free_seq(1)
+    p.free_seq(2)
+    assert p.num_free() == 6 and p.num_cached() == 3
+    _, n = p.add_prompt(3, [1, 2, 3, 4, 9])  # a and b revived, one new block for the tail
+    assert n == 4 and p.blocks(3)[:2] == [a, b] and p.blocks(3)[2] not in (a, b, c)
+    p.free_seq(3)  # a, b freed again (after c)
+    p.add(4)
+    p.append([(4, 8)])  # 4 blocks: the three unhashed free blocks first, then c (least recently freed)
+    assert c not in p.blocks(4)[:3] and p.blocks(4)[3] == c and p.num_cached() == 2
+    p.check_invariants()
+
+
+def test_prompt_that_does_not_fit_changes_nothing():
+    p = BlockPool(3, 4)
+    p.add_prompt(1, list(range(8)))
+    before = (list(p.free), list(p.cached_free), list(p.ref), dict(p.block_of))
+    with pytest.raises(OutOfBlocks):
+        p.add_prompt(2, list(range(100, 112)))
+    assert (list(p.free), list(p.cached_free), list(p.ref), dict(p.block_of)) == before and 2 not in p.seqs
+
+
+class PrefixCacheMachine(RuleBasedStateMachine):
+    """Prompts built from a few shared system prompts and private suffixes; add_prompt / free /
+    fork / append in any order. The cache tokens are not written (slot -1), so the check that
+    every sequence reads its own token ids through its table proves each hit mapped a block
+    holding exactly those tokens."""
+
+    @initialize(N=st.integers(2, 24), B=st.sampled_from([1, 2, 4, 8]), seed=st.integers(0, 1000))
+    def setup(self, N, B, seed):
+        rng = np.random.default_rng(seed)
+        self.pool = BlockPool(N, B, rng.permutation(N))
+        self.systems = [rng.integers(0, 5, size=rng.integers(0, 3 * B + 2)).tolist() for _ in range(3)]
+        self.toks = {}
+        self.content = {}  # slot -> token id
+        self.next = 0
+
+    @rule(data=st.data())
+    def add_prompt(self, data):
+        base = data.draw(st.sampled_from(self.systems))
+        tail = data.draw(st.lists(st.integers(0, 5), max_size=2 * self.pool.block_size))
+        prompt = base + tail
+        try:
+            slots, n_cached = self.pool.add_prompt(self.next, prompt)
+        except OutOfBlocks:
+            return
+        assert all(s == -1 for s in slots[:n_cached]) and all(s >= 0 for s in slots[n_cached:])
+        for s, t in zip(slots, prompt):
+            if s >= 0:
+                self.content[s] = t
+        self.toks[self.next] = list(prompt)
+        self.next += 1
+
+    @precondition(lambda self: self.toks)
+    @rule(data=st.data())
+    def free(self, data):
+        s = data.draw(st.sampled_from(sorted(self.toks)))
+        self.pool.free_seq(s)
+        del self.toks[s]
+
+    @precondition(lambda self: self.toks)
+    @rule(data=st.data())
+    def fork(self, data):
+        s = data.draw(st.sampled_from(sorted(self.toks)))
+        self.pool.fork(s, self.next)
+        self.toks[self.next] = list(self.toks[s])
+        self.next += 1
+
+    @precondition(lambda self: self.toks)
+    @rule(data=st.data())
+    def append(self, data):
+        s = data.draw(st.sampled_from(sorted(self.toks)))
+        new = data.draw(st.lists(st.integers(0, 5), min_size=1, max_size=5))
+        try:
+            slots, pairs = self.pool.append([(s, len(new))])
+        except OutOfBlocks:
+            return
+        B = self.pool.block_size
+        for a, b in pairs:
+            for o in range(B):
+                if a * B + o in self.content:
+                    self.content[b * B + o] = self.content[a * B + o]
+        for sl, t in zip(slots, new):
+            self.content[sl] = t
+        self.toks[s] += new
+
+    @invariant()
+    def consistent_and_every_sequence_reads_its_tokens(self):
+        if not hasattr(self, "pool"):
+            return
+        self.pool.check_invariants()
+        B = self.pool.block_size
+        for s, toks in self.toks.items():
+            blocks = self.pool.blocks(s)
+            assert [self.content.get(blocks[t // B] * B + t % B) for t in range(len(toks))] == toks
+
+
+PrefixCacheMachine.TestCase.settings = settings(max_examples=150, stateful_step_count=40, deadline=None)
+TestPrefixCacheMachine = PrefixCacheMachine.TestCase
+
+
+def test_beam_search_is_a_block_tree():
+    """Slide 14: beam candidates share their common prefix like forked processes. Four beams,
+    each step every beam proposes three continuations (forks), the best four survive (the rest
+    are freed), and each survivor appends its token: the pool holds the tree's distinct blocks,
+    far fewer than four private histories, and every beam reads its own tokens."""
+    B, k = 4, 4
+    p = BlockPool(200, B)
+    rng = np.random.default_rng(5)
+    content = {}
+    p.add(0)
+    slots, _ = p.append([(0, 10)])
+    for s, t in zip(slots, range(10)):
+        content[s] = t
+    hist = {0: list(range(10))}
+    beams, nxt = [0], 1
+    for step in range(12):
+        cands = []
+        for b in beams:
+            for _ in range(3):
+                p.fork(b, nxt)
+                hist[nxt] = list(hist[b])
+                cands.append((float(rng.random()), nxt))
+                nxt += 1
+        for b in beams:
+            p.free_seq(b)
+            del hist[b]
+        cands.sort(reverse=True)
+        beams = [c for _, c in cands[:k]]
+        for _, c in cands[k:]:
+            p.free_seq(c)
+            del hist[c]
+        tok = {b: 100 + step * 10 + i for i, b in enumerate(beams)}
+        slots, pairs = p.append([(b, 1) for b in beams])
+        for a, b2 in pairs:
+            for o in range(B):
+                if a * B + o in content:
+                    content[b2 * B + o] = content[a * B + o]
+        for b, s in zip(beams, slots):
+            content[s] = tok[b]
+            hist[b].append(tok[b])
+        p.check_invariants()
+        for b in beams:
+            bl = p.blocks(b)
+            assert [content[bl[t // B] * B + t % B] for t in range(len(hist[b]))] == hist[b]
+    used = p.num_blocks - p.num_free()
+    private = sum(-(-len(hist[b]) // B) for b in beams)
+    assert used < private, (used, private)
