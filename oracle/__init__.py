@@ -161,6 +161,7 @@ class OracleState:
     step_slots: list = field(default_factory=list)  # slots of each append op, in order
     step_pairs: list = field(default_factory=list)  # copy pairs of each append op, in order
     checks: list = field(default_factory=list)  # attention outputs at each ("check",) op
+    cached_tokens: list = field(default_factory=list)  # prompt tokens found in the prefix cache, per prompt op
 
 
 def batch_tables(pool, batch, pad=-1):
@@ -196,6 +197,12 @@ def replay(w, attend_checks=True, partition_size=None, after_op=None):
             reshape_and_cache(keys, vals, kc, vc, np.array(slots, np.int64), w.block_size)
             st.step_slots.append(slots)
             st.step_pairs.append(pairs)
+        elif kind == "prompt":
+            slots, n_cached = pool.add_prompt(op[1], [int(t) for t in op[2]])
+            reshape_and_cache(op[3], op[4], kc, vc, np.array(slots, np.int64), w.block_size)
+            st.step_slots.append(slots)
+            st.step_pairs.append([])
+            st.cached_tokens.append(n_cached)
         elif kind == "check":
             if attend_checks:
                 tb, ctx = batch_tables(pool, w.batch)

@@ -50,6 +50,15 @@ class PagedKVCache:
     def free(self, sid):
         self.pool.free(sid)
 
+    def add_prompt(self, sid, tokens, keys, values):
+        """Add sequence sid with its prompt through the prefix cache: keys/values [n, Hkv, D] device
+        tensors for the whole prompt; rows of cached tokens are not written. Returns n_cached."""
+        slots, n_cached = self.pool.add_prompt(sid, tokens)
+        self.last_slots, self.last_pairs = slots, np.zeros((0, 2), np.int32)
+        if len(slots) > n_cached:
+            kernels.reshape_and_cache(keys, values, self.k, self.v, torch.from_numpy(slots).to(self.device))
+        return n_cached
+
     def append(self, sids, keys, values):
         """Append keys[i]/values[i] ([n_i, Hkv, D] device tensors) to sequence sids[i], all or nothing.
 
@@ -90,7 +99,8 @@ def to_device(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
 
 def run_ops(cache: PagedKVCache, ops, dtype, on_check=None):
     """Replay a list of scheduler operations:
-    ("add", sid) | ("fork", parent, child) | ("free", sid) | ("append", [(sid, k, v), ...]) | ("check",).
+    ("add", sid) | ("fork", parent, child) | ("free", sid) | ("append", [(sid, k, v), ...]) | ("check",)
+    | ("prompt", sid, token_ids, k, v) (a sequence added with its whole prompt through the prefix cache).
     k, v are host storage arrays [n, Hkv, D]. on_check() is called at each ("check",)."""
     for op in ops:
         kind = op[0]
@@ -109,6 +119,8 @@ def run_ops(cache: PagedKVCache, ops, dtype, on_check=None):
             ks = list(torch.split(keys, counts))
             vs = list(torch.split(vals, counts))
             cache.append(sids, ks, vs)
+        elif kind == "prompt":
+            cache.add_prompt(op[1], op[2], to_device(op[3], dtype, cache.device), to_device(op[4], dtype, cache.device))
         elif kind == "check":
             if on_check is not None:
                 on_check()

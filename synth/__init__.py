@@ -25,6 +25,7 @@ import numpy as np
 
 # stream tags
 _LENGTHS, _FREE, _Q, _KV, _PREFIX, _PROMPT = 1, 2, 3, 4, 5, 6
+_SYSTEM, _SYSKV, _TOKENS = 7, 8, 9
 
 DTYPES = ("f32", "f16", "bf16")
 ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -308,6 +309,44 @@ def parallel_sampling(seed=3, prompts=8, n=4, prompt_len=512, max_extra=15, max_
                     scale=float(np.float32(1.0 / math.sqrt(d))), partition_size=0, ops=ops,
                     batch=list(range(S)), q=q, lmax=int((L0[:, None] + pb).max()), value_scale=0.5,
                     notes={"s_p": sp.tolist(), "private": pb.tolist(), "steps": steps, "checks": checks})
+
+
+def prefix_cache_requests(seed=6, system_lens=(69, 128, 200), requests=12, private=(1, 100), hq=16, hkv=8,
+                          d=128, block_size=16, dtype="f16", vocab=32000):
+    """Requests that open with one of a few shared system prompts (the lesson note, section
+    3.1), each added with its whole prompt through the prefix cache, some freed as later ones
+    arrive (so cached blocks are found again after falling free), then one decode step.
+
+    A system prompt's token ids and its keys/values are drawn per (system prompt, position), so
+    every request that opens with it carries the same rows there; the private part is drawn per
+    request. Op ("prompt", sid, token_ids, k, v) adds a sequence with its whole prompt."""
+    r = _rng(seed, _LENGTHS)
+    kinds = r.integers(0, len(system_lens), size=requests)
+    plen = r.integers(private[0], private[1] + 1, size=requests)
+    sys_tok = [_rng(seed, _SYSTEM, s).integers(0, vocab, size=L).astype(np.int32) for s, L in enumerate(system_lens)]
+    sys_kv = _draw_kv(seed, _SYSKV, [(s,) for s in range(len(system_lens))], list(system_lens), hkv, d, 0.5, dtype)
+    prv_kv = _draw_kv(seed, _KV, [(i,) for i in range(requests)], [int(x) + 1 for x in plen], hkv, d, 0.5, dtype)
+    ops, live = [], []
+    for i in range(requests):
+        s = int(kinds[i])
+        toks = np.concatenate([sys_tok[s], _rng(seed, _TOKENS, i).integers(0, vocab, size=int(plen[i])).astype(np.int32)])
+        k = np.concatenate([sys_kv[s][0], prv_kv[i][0][:-1]])
+        v = np.concatenate([sys_kv[s][1], prv_kv[i][1][:-1]])
+        ops.append(("prompt", i, toks, k, v))
+        live.append(i)
+        if i % 4 == 3:  # a request finishes: its blocks fall free, the hashed ones stay cached
+            gone = live.pop(1)
+            ops.append(("free", gone))
+    ops.append(("append", [(i, prv_kv[i][0][-1:], prv_kv[i][1][-1:]) for i in live]))
+    need = sum(-(-(system_lens[int(kinds[i])] + int(plen[i]) + 1) // block_size) for i in range(requests))
+    nb = _pool_size(need)
+    free_order = _rng(seed, _FREE).permutation(nb).astype(np.int32)
+    q = normal(_rng(seed, _Q), (len(live), hq, d), 0.5, dtype)
+    return Workload(name="prefix-cache", dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                    block_size=block_size, num_blocks=nb, free_order=free_order,
+                    scale=float(np.float32(1.0 / math.sqrt(d))), partition_size=0, ops=ops, batch=live, q=q,
+                    lmax=int(max(system_lens) + private[1] + 1), value_scale=0.5,
+                    notes={"kinds": kinds.tolist(), "private": plen.tolist()})
 
 
 def kv_bytes_per_token(num_kv_heads, head_dim, elt_bytes):

@@ -404,3 +404,26 @@ def test_peaked_softmax_and_large_values(dtype, hq, hkv, d):
         err = assert_close(gpu_attention(c, w, partition_size=P), ref, dtype, f"peaked {dtype} P={P}",
                            storage_ulp=True)
         say(f"  [peaked {dtype} Hq={hq} Hkv={hkv}] P={P} max abs err {err:.3e}")
+
+
+def test_prefix_cache_requests():
+    """Requests opening with shared system prompts go through the prefix cache: the GPU side
+    writes only the uncached prompt tokens, its pools stay byte-identical to the oracle's, the
+    same prompt tokens were found cached, and attention matches the oracle."""
+    w = synth.prefix_cache_requests()
+    st = oracle.replay(w)
+    cached = []
+    dt = TORCH_DTYPE[w.dtype]
+    c = PagedKVCache(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, dt, free_order=w.free_order)
+    from paged_kv_cache_416_amd.cache import run_ops
+    for op in w.ops:
+        run_ops(c, [op], dt)
+        if op[0] == "prompt":
+            cached.append(int((c.last_slots < 0).sum()))
+    torch.cuda.synchronize()
+    assert cached == st.cached_tokens and sum(cached) > 0
+    same_bytes(cache_bytes(c.k), host_bytes(st.k_cache), "prefix-cache K")
+    same_bytes(cache_bytes(c.v), host_bytes(st.v_cache), "prefix-cache V")
+    ref = oracle.attention_of(st, w)
+    for P in (0, BALANCED):
+        assert_close(gpu_attention(c, w, partition_size=P), ref, w.dtype, f"prefix-cache P={P}")

@@ -87,3 +87,25 @@ def test_full_size_recipe_shapes():
     blocks = sum(-(-int(c) // 16) for c in lens)
     assert 30 * 128 / 16 <= blocks <= 30 * 128
     assert math.ceil(1.1 * blocks) > blocks
+
+
+def test_prefix_cache_requests_read_their_own_rows():
+    """Prefix-cache workload: cached prompt tokens are never written, yet every live request's
+    attention through the oracle's cache equals dense attention over that request's own prompt
+    and decode rows (float64, 1e-12), and later requests did find their system prompt's blocks."""
+    w = synth.prefix_cache_requests()
+    st = oracle.replay(w)
+    assert sum(st.cached_tokens) > 0 and st.cached_tokens[0] == 0
+    ref = oracle.attention_of(st, w)
+    rows = {op[1]: (op[3], op[4]) for op in w.ops if op[0] == "prompt"}
+    last = {sid: (k, v) for sid, k, v in w.ops[-1][1]}
+    q = synth.storage_to_f64(w.q, w.dtype)
+    G = w.num_q_heads // w.num_kv_heads
+    for i, sid in enumerate(w.batch):
+        k = synth.storage_to_f64(np.concatenate([rows[sid][0], last[sid][0]]), w.dtype)
+        v = synth.storage_to_f64(np.concatenate([rows[sid][1], last[sid][1]]), w.dtype)
+        for h in range(w.num_q_heads):
+            x = np.float64(w.scale) * (k[:, h // G, :] @ q[i, h])
+            p = np.exp(x - x.max())
+            dense = (p[:, None] * v[:, h // G, :]).sum(0) / p.sum()
+            assert np.allclose(ref[i, h], dense, rtol=1e-12, atol=1e-14)
