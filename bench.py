@@ -91,6 +91,7 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
+    ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
@@ -310,6 +311,9 @@ def main():
     if args.swap:
         result["swap"] = swap_leg(cache, w, dev, dt)
 
+    if args.prefix_cache:
+        result["prefix_cache"] = prefix_cache_leg()
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.workload, P, unique_b, args.cpu_seconds)
 
@@ -363,6 +367,31 @@ def swap_leg(cache, w, dev, dt, reps=5):
             "in_us": round(in_us, 1), "in_GB/s": round(nbytes / in_us / 1e3, 1),
             "runtime_copy_GB/s": {"device_to_host": round(nbytes / d2h / 1e3, 1),
                                   "host_to_device": round(nbytes / h2d / 1e3, 1)}}
+
+
+def prefix_cache_leg(requests=256, system=1024, seed=11):
+    """Host cost of the prefix cache at the 8B-shaped GQA workload's shape: `requests` prompts
+    opening with one shared `system`-token prompt plus lognormal private tails, added through
+    pkv_seq_add_prompt (chained SHA-256 per full block, lookup, allocation)."""
+    import numpy as np
+
+    from paged_kv_cache_416_amd import Pool
+    rng = np.random.default_rng(seed)
+    tails = np.clip(np.round(np.exp(rng.normal(np.log(1024), 1.0, size=requests))), 1, 8192).astype(np.int64)
+    sys_toks = rng.integers(0, 128000, size=system).astype(np.int32)
+    prompts = [np.concatenate([sys_toks, rng.integers(0, 128000, size=int(t)).astype(np.int32)]) for t in tails]
+    B = 16
+    pool = Pool(int(sum(-(-len(p) // B) for p in prompts)) + 8, B)
+    cached = 0
+    t0 = time.perf_counter()
+    for i, p in enumerate(prompts):
+        _, n = pool.add_prompt(i, p)
+        cached += n
+    t = time.perf_counter() - t0
+    total = int(sum(len(p) for p in prompts))
+    return {"requests": requests, "prompt_tokens": total, "cached_tokens": cached,
+            "cached_fraction": round(cached / total, 4), "host_us_per_request": round(1e6 * t / requests, 1),
+            "hashed_MB_per_s": round(total * 4 / t / 1e6, 1)}
 
 
 def read_probe_leg(nbytes, args, dev):
