@@ -53,8 +53,10 @@ def lib():
         L.oracle_paged_attention.argtypes = [_p, _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                              _f64, _i32, _i32]
         L.oracle_contiguous_attention.argtypes = [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _f64, _i32]
+        L.oracle_paged_prefill.argtypes = [_p, _p, _p, _p, _i64, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                           _f64, _i32]
         for f in (L.oracle_decode_element, L.oracle_reshape_and_cache, L.oracle_copy_blocks,
-                  L.oracle_paged_attention, L.oracle_contiguous_attention, L.oracle_threads):
+                  L.oracle_paged_attention, L.oracle_contiguous_attention, L.oracle_paged_prefill, L.oracle_threads):
             f.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -122,6 +124,26 @@ def paged_attention(q, k_cache, v_cache, tables, ctx, scale, dtype, partition_si
                                       float(scale), int(partition_size), DTYPE_CODE[dtype])
     if rc:
         raise ValueError(f"oracle_paged_attention failed ({rc})")
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, tables, ctx, query_start, scale, dtype):
+    """q [T, Hq, D] (rows query_start[s]..query_start[s+1]-1 are sequence s's last queries, causal
+    over its ctx[s] keys); caches [N, Hkv, B, D]; tables int32 [S, max_blocks] -> float64 [T, Hq, D]."""
+    T, hq, d = q.shape
+    N, hkv, B, d2 = k_cache.shape
+    assert d == d2
+    tables = np.ascontiguousarray(tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    assert qs[-1] == T
+    out = np.zeros((T, hq, d), np.float64)
+    qr, kr, vr = _raw(q, dtype), _raw(k_cache, dtype), _raw(v_cache, dtype)
+    rc = lib().oracle_paged_prefill(_ptr(out), _ptr(qr), _ptr(kr), _ptr(vr), N, _ptr(tables),
+                                    tables.shape[1] if tables.ndim == 2 else 0, _ptr(ctx), _ptr(qs), len(ctx), hq,
+                                    hkv, d, B, float(scale), DTYPE_CODE[dtype])
+    if rc:
+        raise ValueError(f"oracle_paged_prefill failed ({rc})")
     return out
 
 

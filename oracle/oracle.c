@@ -293,6 +293,59 @@ int oracle_paged_attention(double *out, const void *q, const void *k_cache, cons
 }
 
 /*
+ * Prefill (chunked) attention over the paged cache, in double precision: sequence s holds
+ * context_lens[s] tokens, of which the last n_s = query_start[s+1] - query_start[s] are
+ * queries (rows query_start[s] .. query_start[s+1]-1 of q and out, [T][num_q_heads][head_dim]).
+ * Query i of s sits at position p = context_lens[s] - n_s + i and attends, causally, to the
+ * keys at positions 0 .. p ("vLLM and PagedAttention" slide 3: the prompt is processed in
+ * parallel; the cache holds every earlier token, shared prefix blocks included).
+ */
+int oracle_paged_prefill(double *out, const void *q, const void *k_cache, const void *v_cache, int64_t num_blocks,
+                         const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens,
+                         const int32_t *query_start, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, double scale, int32_t dtype)
+{
+    if (num_seqs < 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 ||
+        dtype < 0 || dtype > 2)
+        return ORC_EINVAL;
+    if (check_tables(block_tables, max_blocks, context_lens, num_seqs, block_size, num_blocks))
+        return ORC_EINVAL;
+    int32_t max_ctx = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = query_start[s + 1] - query_start[s];
+        if (n < 0 || n > context_lens[s]) return ORC_EINVAL;
+        if (context_lens[s] > max_ctx) max_ctx = context_lens[s];
+    }
+    const int32_t G = num_q_heads / num_kv_heads;
+    const int64_t T = query_start[num_seqs];
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * ((size_t)max_ctx + 1));
+        if (!x) {
+#pragma omp atomic write
+            err = ORC_ENOMEM;
+        }
+#pragma omp for collapse(2) schedule(dynamic, 4)
+        for (int64_t r = 0; r < T; ++r) {
+            for (int32_t h = 0; h < num_q_heads; ++h) {
+                if (!x) continue;
+                int32_t s = 0;
+                while (query_start[s + 1] <= r) ++s;
+                const int64_t pos = (int64_t)context_lens[s] - (query_start[s + 1] - query_start[s]) + (r - query_start[s]);
+                struct paged_rows rc = {block_tables + (int64_t)s * max_blocks, h / G, num_kv_heads, block_size,
+                                        head_dim};
+                const int64_t off = (r * num_q_heads + h) * head_dim;
+                attend_one(out + off, q, off, k_cache, v_cache, paged_row, &rc, 0, pos + 1, head_dim, scale, dtype, x,
+                           NULL, NULL);
+            }
+        }
+        free(x);
+    }
+    return err;
+}
+
+/*
  * The same attention over a contiguous cache k, v: [num_seqs][num_kv_heads][lmax][head_dim];
  * token t of (s, kv head) is row t of that slab.
  */

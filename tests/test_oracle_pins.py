@@ -396,3 +396,49 @@ def test_copy_blocks_whole_block_bytes():
     assert np.array_equal(kc[0], k0[3]) and np.array_equal(vc[0], v0[3])
     for b in (1, 2, 3, 5):
         assert np.array_equal(kc[b], k0[b]) and np.array_equal(vc[b], v0[b])
+
+
+# ---------------------------------------------------------------- prefill (chunked, causal)
+
+@settings(max_examples=40, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1), S=st.integers(1, 3), hkv=st.integers(1, 2), G=st.sampled_from([1, 2, 4]),
+       d=st.sampled_from([8, 16]), B=st.sampled_from([1, 4, 16]), max_ctx=st.integers(1, 48),
+       dtype=st.sampled_from(["f32", "bf16"]))
+def test_paged_prefill_equals_library_causal_sdpa(seed, S, hkv, G, d, B, max_ctx, dtype):
+    """Each sequence's last n_s tokens as queries, causal over its whole context (earlier tokens
+    included): the oracle equals torch's scaled_dot_product_attention in float64 with an explicit
+    boolean mask (query at position p sees keys 0..p), the cases placed into blocks by numpy."""
+    rng = np.random.default_rng(seed)
+    hq = hkv * G
+    _, ks, vs, kc, vc, tables, ctx = _random_case(rng, S, hq, hkv, d, B, max_ctx, dtype)
+    n = np.array([int(rng.integers(0, c + 1)) for c in ctx], np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = synth.normal(rng, (int(qs[-1]), hq, d), 1.0, dtype)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    got = oracle.paged_prefill(q, kc, vc, tables, ctx, qs, scale, dtype)
+    for s in range(S):
+        if n[s] == 0:
+            continue
+        k = np.repeat(synth.storage_to_f64(ks[s], dtype).transpose(1, 0, 2), G, axis=0)[None]  # [1, Hq, T, D]
+        v = np.repeat(synth.storage_to_f64(vs[s], dtype).transpose(1, 0, 2), G, axis=0)[None]
+        qq = synth.storage_to_f64(q[qs[s]:qs[s + 1]], dtype).transpose(1, 0, 2)[None]  # [1, Hq, n, D]
+        pos = ctx[s] - n[s] + np.arange(n[s])
+        mask = torch.from_numpy(pos[:, None] >= np.arange(ctx[s])[None, :])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qq), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(got[qs[s]:qs[s + 1]], ref[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_of_one_query_is_decode_and_whole_prompt_is_causal():
+    """n_s = 1 is decode attention; a fresh prompt (n_s = ctx) has its first query return its
+    own value row exactly (one key)."""
+    rng = np.random.default_rng(3)
+    q1, ks, vs, kc, vc, tables, ctx = _random_case(rng, 3, 4, 2, 16, 4, 30, "f32")
+    one = oracle.paged_prefill(q1, kc, vc, tables, ctx, np.arange(4, dtype=np.int32), 0.25, "f32")
+    np.testing.assert_array_equal(one, oracle.paged_attention(q1, kc, vc, tables, ctx, 0.25, "f32"))
+    qs = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    qa = synth.normal(rng, (int(qs[-1]), 4, 16), 1.0, "f32")
+    full = oracle.paged_prefill(qa, kc, vc, tables, ctx, qs, 0.25, "f32")
+    for s in range(3):
+        first = synth.storage_to_f64(vs[s][0], "f32")  # [Hkv, D]
+        np.testing.assert_array_equal(full[qs[s]], np.repeat(first, 2, axis=0))
