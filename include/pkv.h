@@ -269,6 +269,30 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
                                float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
                                int32_t dtype, uint32_t flags, hipStream_t stream);
 
+/* Prefill (chunked) attention over the paged cache: the last n_s = query_start[s+1] -
+ * query_start[s] tokens of each sequence s are queries, and query i of s, at position
+ * p = context_lens[s] - n_s + i, attends causally to the keys at positions 0 .. p, earlier
+ * chunks and shared prefix blocks included (slide 3: the prompt is processed in parallel;
+ * slides 9 and 10: keys and values fetched block by block through the block table). The
+ * queries' own keys and values must already be in the cache (pkv_reshape_and_cache).
+ *   out[r][h] = softmax_t(scale * q[r][h] . K_t) . V_t over t <= p, for row r = query_start[s] + i
+ *  out, q: [query_start[num_seqs]][num_q_heads][head_dim], dtype, out written with RNE.
+ *  query_start: device int32[num_seqs + 1], query_start[0] = 0, non-decreasing;
+ *               n_s <= context_lens[s]; max_query_len: host bound on n_s (sizes the launch).
+ *  block_tables, context_lens, max_context_len, scale: as for pkv_paged_attention_decode.
+ *  flags: 0.
+ * The grouped-query matrix-core kernel generalised: a wave owns 16 (query token, query head)
+ * rows of one kv head and walks every key tile up to its last row's position.
+ * Supported: f16/bf16, head_dim 128, block_size 16 or 32, num_q_heads a multiple of
+ * num_kv_heads. A sequence with n_s > context_lens[s] gets no output (a caller error;
+ * PKV_DEBUG_VALIDATE=1 reports it, with the checks of the decode call, as PKV_EINVAL). */
+int pkv_paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *context_lens, const int32_t *query_start, int32_t max_query_len,
+                                int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, float scale, int32_t dtype, uint32_t flags,
+                                hipStream_t stream);
+
 /* The same attention over a contiguous cache, the layout paging replaces (slide 19 prices
  * the indirection against it): k, v are [num_seqs][num_kv_heads][lmax][head_dim] and token t
  * of (s, kv head) is row t of that slab. Same kernels, same tiling; only the address of a

@@ -70,6 +70,24 @@ int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_
     return PKV_OK;
 }
 
+int validate_query_start(const char *fn, const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,
+                         int32_t max_query_len, hipStream_t stream) {
+    std::vector<int32_t> qs, ctx;
+    int rc = fetch(fn, "query_start", query_start, static_cast<size_t>(num_seqs) + 1, stream, qs);
+    if (rc) return rc;
+    rc = fetch(fn, "context_lens", context_lens, static_cast<size_t>(num_seqs), stream, ctx);
+    if (rc) return rc;
+    if (qs[0] != 0) return fail(PKV_EINVAL, "%s: query_start[0] = %d, not 0 (PKV_DEBUG_VALIDATE)", fn, qs[0]);
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = qs[s + 1] - qs[s];
+        if (n < 0 || n > max_query_len || n > ctx[s])
+            return fail(PKV_EINVAL,
+                        "%s: sequence %d has %d queries (max_query_len %d, context %d) (PKV_DEBUG_VALIDATE)", fn, s, n,
+                        max_query_len, ctx[s]);
+    }
+    return PKV_OK;
+}
+
 int validate_slots(const char *fn, const int64_t *slot_mapping, int32_t num_tokens, int64_t num_slots,
                    hipStream_t stream) {
     std::vector<int64_t> slots;
