@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
     ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
+    ap.add_argument("--prefill", type=int, default=0, metavar="PROMPT_LEN",
+                    help="also time paged prefill of 8 prompts of this length (8B shape)")
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
@@ -314,6 +316,9 @@ def main():
     if args.prefix_cache:
         result["prefix_cache"] = prefix_cache_leg()
 
+    if args.prefill:
+        result["prefill"] = prefill_leg(dev, args.prefill)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.workload, P, unique_b, args.cpu_seconds)
 
@@ -392,6 +397,41 @@ def prefix_cache_leg(requests=256, system=1024, seed=11):
     return {"requests": requests, "prompt_tokens": total, "cached_tokens": cached,
             "cached_fraction": round(cached / total, 4), "host_us_per_request": round(1e6 * t / requests, 1),
             "hashed_MB_per_s": round(total * 4 / t / 1e6, 1)}
+
+
+def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=10):
+    """Paged prefill at the 8B shape: `seqs` fresh prompts of `prompt_len` tokens, every token a
+    causal query over the paged cache (random placement). Algorithmic flops: 4 d per (query,
+    visible key, query head): q.k and p.v."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_416_amd import kernels
+    rng = np.random.default_rng(21)
+    nb_seq = -(-prompt_len // B)
+    N = seqs * nb_seq + 16
+    perm = rng.permutation(N).astype(np.int32)
+    tables = torch.from_numpy(perm[:seqs * nb_seq].reshape(seqs, nb_seq).copy()).to(dev)
+    k = (torch.randn(N, hkv, B, d, device=dev) * 0.5).to(torch.bfloat16)
+    v = (torch.randn(N, hkv, B, d, device=dev) * 0.5).to(torch.bfloat16)
+    ctx = torch.full((seqs,), prompt_len, dtype=torch.int32, device=dev)
+    qs = torch.arange(0, (seqs + 1) * prompt_len, prompt_len, dtype=torch.int32, device=dev)
+    q = (torch.randn(seqs * prompt_len, hq, d, device=dev) * 0.5).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def run(i):
+        kernels.paged_attention_prefill(out, q, k, v, tables, ctx, qs, prompt_len, prompt_len, d ** -0.5)
+
+    for i in range(3):
+        run(i)
+    us = timed_launches(run, reps, stream)
+    flops = 4 * d * hq * seqs * prompt_len * (prompt_len + 1) / 2
+    tf = flops / (us * 1e-6) / 1e12
+    return {"sequences": seqs, "prompt_len": prompt_len, "q_heads": hq, "kv_heads": hkv, "dtype": "bf16",
+            "us": round(us, 1), "TFLOP/s": round(tf, 1), "roofline": {"bound": "mfma", "peak": 2500.0,
+                                                                       "frac": round(tf / 2500.0, 4)},
+            "tokens_per_s": round(seqs * prompt_len / (us * 1e-6), 0)}
 
 
 def read_probe_leg(nbytes, args, dev):

@@ -21,6 +21,7 @@ namespace {
 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillStages = 2;
+constexpr int kPrefillRowTiles = 2;  // 16-row tiles per wave, sharing each key/value tile it loads
 
 struct PrefillParams {
     void *out;
@@ -31,7 +32,7 @@ struct PrefillParams {
     float scale_log2;
 };
 
-template <class E, int B, int W>
+template <class E, int B, int W, int RT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const PrefillParams p) {
     using M = Mfma<E>;
@@ -48,27 +49,33 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int nq = __builtin_amdgcn_readfirstlane(p.query_start[s + 1]) - q0;
     const int ctx = clamp_ctx(__builtin_amdgcn_readfirstlane(p.ctx_lens[s]), p.ctx_cap);
     const int rows = nq * G;
-    const int row0 = (blockIdx.x * W + wave) * 16;
+    const int row0 = (blockIdx.x * W + wave) * 16 * RT;  // the wave's RT row tiles start here
     if (nq <= 0 || nq > ctx || row0 >= rows) return;  // uniform over the wave
 
-    // row n of the tile: query token, head, position
-    const int r = row0 + n;
-    const bool row_ok = r < rows;
-    const int tok = row_ok ? r / G : 0;
-    const int head = kvh * G + (row_ok ? r % G : 0);
-    const int qpos = ctx - nq + tok;
-    const int last_tok = (min(row0 + 15, rows - 1)) / G;
-    // keys this tile needs: [0, kend) (uniform: it sizes the loop and the buffer resources)
+    // row n of each of the wave's row tiles: query token, head, position
+    bool row_ok[RT];
+    int tok[RT], head[RT], qpos[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = row0 + rt * 16 + n;
+        row_ok[rt] = r < rows;
+        tok[rt] = row_ok[rt] ? r / G : 0;
+        head[rt] = kvh * G + (row_ok[rt] ? r % G : 0);
+        qpos[rt] = ctx - nq + tok[rt];
+    }
+    const int last_tok = (min(row0 + 16 * RT - 1, rows - 1)) / G;
+    // keys these rows need: [0, kend) (uniform: it sizes the loop and the buffer resources)
     const int kend = __builtin_amdgcn_readfirstlane(ctx - nq + last_tok + 1);
     const int ntile = (kend + TR - 1) / TR;
 
-    u32x4 qv[4];
-    {
+    u32x4 qv[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
         const char *qp = static_cast<const char *>(p.q) +
-                         ((static_cast<int64_t>(q0 + tok) * p.num_q_heads + head) * D + g * 8) * 2;
+                         ((static_cast<int64_t>(q0 + tok[rt]) * p.num_q_heads + head[rt]) * D + g * 8) * 2;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            qv[kk] = row_ok ? *reinterpret_cast<const u32x4 *>(qp + kk * 64) : u32x4{0u, 0u, 0u, 0u};
+            qv[rt][kk] = row_ok[rt] ? *reinterpret_cast<const u32x4 *>(qp + kk * 64) : u32x4{0u, 0u, 0u, 0u};
     }
 
     TableEntry *trow = (TableEntry *)(p.tables + static_cast<int64_t>(s) * p.max_blocks);  // address-space cast
@@ -100,48 +107,57 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         cpb = trow[min(ct, ntile - 1) / SPB];
     };
 
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 acc[8];
+    float m[RT], lsum[RT];
+    f32x4 acc[RT][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = -INFINITY;
+        lsum[rt] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
+    // one key tile against every row tile of the wave (the tile's loads serve RT * 16 rows)
     auto consume = [&](Stage &S) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[kk], qv[kk], c);
-        float sc[4], mloc = -INFINITY;
+        for (int rt = 0; rt < RT; ++rt) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kpos = S.t * TR + 4 * g + i;  // a stand-in's keys all lie past kend
-            const bool valid = S.ok && kpos <= qpos && kpos < kend;
-            sc[i] = valid ? c[i] * p.scale_log2 : -INFINITY;
-            mloc = fmaxf(mloc, sc[i]);
+            for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[kk], qv[rt][kk], c);
+            float sc[4], mloc = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kpos = S.t * TR + 4 * g + i;  // a stand-in's keys all lie past kend
+                const bool valid = S.ok && kpos <= qpos[rt] && kpos < kend;
+                sc[i] = valid ? c[i] * p.scale_log2 : -INFINITY;
+                mloc = fmaxf(mloc, sc[i]);
+            }
+            mloc = max_over_lane_groups(mloc);
+            const float m_new = fmaxf(m[rt], mloc);
+            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+            if (__builtin_amdgcn_ballot_w64(m_new > m[rt]) != 0) {
+                const float alpha = fast_exp2(m[rt] - m_ref);
+                lsum[rt] *= alpha;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[rt][j] *= alpha;
+            }
+            const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
+            const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
+            const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
+            const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
+            const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
+            lsum[rt] = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum[rt]))));
+            const u32x2 ph = {h01, h23}, pr = {r01, r23};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int w = j >> 1;
+                const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[1], w), word(S.v[0], w), sel),
+                                  __builtin_amdgcn_perm(word(S.v[3], w), word(S.v[2], w), sel)};
+                acc[rt][j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[rt][j]));
+            }
+            m[rt] = m_new;
         }
-        mloc = max_over_lane_groups(mloc);
-        const float m_new = fmaxf(m, mloc);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-            const float alpha = fast_exp2(m - m_ref);
-            lsum *= alpha;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-        }
-        const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
-        const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
-        const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
-        const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
-        const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
-        lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
-        const u32x2 ph = {h01, h23}, pr = {r01, r23};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int w = j >> 1;
-            const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[1], w), word(S.v[0], w), sel),
-                              __builtin_amdgcn_perm(word(S.v[3], w), word(S.v[2], w), sel)};
-            acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
-        }
-        m = m_new;
     };
 
     // ring of NS stages over the wave's key tiles; whole rounds, the end tested at a round's
@@ -163,25 +179,29 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     }
 
-    // row n's weight sum over the four lane groups; lane (n, g) holds d = 8 (4g + i) + j
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (row_ok) {
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        const int64_t base = (static_cast<int64_t>(q0 + tok) * p.num_q_heads + head) * D;
+    // each row's weight sum over the four lane groups; lane (n, g) holds d = 8 (4g + i) + j
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int rt = 0; rt < RT; ++rt) {
+        float l = lsum[rt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (row_ok[rt]) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const int64_t base = (static_cast<int64_t>(q0 + tok[rt]) * p.num_q_heads + head[rt]) * D;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) E::store(p.out, base + 8 * (4 * g + i) + j, acc[j][i] * inv);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) E::store(p.out, base + 8 * (4 * g + i) + j, acc[rt][j][i] * inv);
+        }
     }
 }
 
 template <class E, int B>
 int launch(const PrefillParams &p, int32_t max_query_len, int32_t num_seqs, hipStream_t stream) {
     const int64_t tiles = ceil_div(static_cast<int64_t>(max_query_len) * p.group, 16);
-    const int64_t gx = ceil_div(tiles, kPrefillWaves);
+    const int64_t gx = ceil_div(tiles, kPrefillWaves * kPrefillRowTiles);
     if (gx > INT32_MAX) return fail(PKV_EINVAL, "pkv_paged_attention_prefill: max_query_len too large");
-    hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves>), dim3(static_cast<unsigned>(gx), p.num_kv_heads, num_seqs),
+    hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles>), dim3(static_cast<unsigned>(gx), p.num_kv_heads, num_seqs),
                        dim3(kPrefillWaves * 64), 0, stream, p);
     return hip_status(hipGetLastError(), "pkv_paged_attention_prefill launch");
 }
