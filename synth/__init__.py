@@ -26,6 +26,7 @@ import numpy as np
 # stream tags
 _LENGTHS, _FREE, _Q, _KV, _PREFIX, _PROMPT = 1, 2, 3, 4, 5, 6
 _SYSTEM, _SYSKV, _TOKENS = 7, 8, 9
+_REQUESTS = 10
 
 DTYPES = ("f32", "f16", "bf16")
 ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -347,6 +348,22 @@ def prefix_cache_requests(seed=6, system_lens=(69, 128, 200), requests=12, priva
                     scale=float(np.float32(1.0 / math.sqrt(d))), partition_size=0, ops=ops, batch=live, q=q,
                     lmax=int(max(system_lens) + private[1] + 1), value_scale=0.5,
                     notes={"kinds": kinds.tolist(), "private": plen.tolist()})
+
+
+def serving_requests(seed=7, n=2000, prompt_median=160, output_median=200, sigma=1.0, max_context=2048,
+                     rate=None):
+    """Request lengths and arrival steps for the memory simulator: prompt and output lengths
+    log-normal around the given medians, prompt + output within max_context (the reservation
+    of the contiguous scheme, lesson note section 1), arrivals a Poisson process of `rate`
+    requests per step (None: all at step 0). Returns int32 arrays (arrival, prompt, output)."""
+    r = _rng(seed, _REQUESTS)
+    prompt = np.clip(np.rint(r.lognormal(math.log(prompt_median), sigma, n)), 1, max_context - 1).astype(np.int64)
+    output = np.clip(np.rint(r.lognormal(math.log(output_median), sigma, n)), 1, max_context - prompt).astype(np.int64)
+    if rate is None:
+        arrival = np.zeros(n, np.int64)
+    else:
+        arrival = np.floor(np.cumsum(r.exponential(1.0 / rate, n))).astype(np.int64)
+    return arrival.astype(np.int32), prompt.astype(np.int32), output.astype(np.int32)
 
 
 def kv_bytes_per_token(num_kv_heads, head_dim, elt_bytes):
