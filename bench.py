@@ -42,7 +42,7 @@ COUNTERS = {
                    [CSRC + "attention.hip", CSRC + "attention.h", CSRC + "common.h"],
                    "attn_decode_kernel", 0, 0),
     "8b-gqa-prefix": ("attn_gqa_bf16_8b_balanced_counters.txt",
-                      [CSRC + "attention_gqa.hip", CSRC + "attention.h", CSRC + "common.h"],
+                      [CSRC + "attention_gqa.hip", CSRC + "mfma.h", CSRC + "attention.h", CSRC + "common.h"],
                       "attn_gqa_balanced_kernel", PARTITION_BALANCED, FLAG_CACHED_KV),
 }
 
