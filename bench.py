@@ -94,6 +94,8 @@ def parse():
     ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
     ap.add_argument("--prefill", type=int, default=0, metavar="PROMPT_LEN",
                     help="also time paged prefill of 8 prompts of this length (8B shape)")
+    ap.add_argument("--memory-sim", action="store_true",
+                    help="host only: run the continuous-batching memory simulator and print its JSON line")
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
@@ -189,6 +191,9 @@ def main():
         return summarize_counters(*args.summarize_counters)
     if args.cpu_one_thread:
         return cpu_one_thread(args.cpu_one_thread[0], int(args.cpu_one_thread[1]))
+    if args.memory_sim:
+        print(json.dumps(memory_sim_leg()))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The path shards by sequence or by "
               f"KV head with no exchange between GPUs, so one GPU's figure at its share of the batch is the "
@@ -397,6 +402,68 @@ def prefix_cache_leg(requests=256, system=1024, seed=11):
     return {"requests": requests, "prompt_tokens": total, "cached_tokens": cached,
             "cached_fraction": round(cached / total, 4), "host_us_per_request": round(1e6 * t / requests, 1),
             "hashed_MB_per_s": round(total * 4 / t / 1e6, 1)}
+
+
+# Memory of one token's keys and values in a 13B-class model, fp16: 2 (K, V) x 5120 x 40 layers x 2 B
+# (slide 5 of the "vLLM and PagedAttention" deck).
+KV_TOKEN_BYTES_13B = 2 * 5120 * 40 * 2
+
+
+def memory_sim_leg(seed=7, block_size=16, reserve=2048, oracle_requests=400):
+    """Continuous-batching memory simulator (host only) on two memory budgets for a 13B-class
+    model: the pages' device (30 % of 40 GB for keys and values, slide 4) and one MI355X (288 GB
+    less 26 GB of fp16 weights and 10 GB kept for activations). The same seeded requests
+    (log-normal prompt and output lengths, medians 160 and 200 tokens, within a 2048-token
+    context) all wait at step 0; the contiguous scheme reserves the whole 2048-token context per
+    request (the lesson note's example), the paged scheme takes 16-slot blocks with 1 % of the
+    pool kept free at admission. Reports the useful share of held memory, the batch size, the
+    native simulator's cost per step, and the oracle simulator timed beside it on a sample."""
+    import numpy as np
+
+    import synth
+    from oracle import simulator as ref
+    from paged_kv_cache_416_amd import sim
+    configs = []
+    for name, kv_bytes, n, max_batch in (("40GB-device-13B", 0.30 * 40e9, 2000, 256),
+                                         ("mi355x-288GB-13B", 288e9 - 26e9 - 10e9, 20000, 4096)):
+        blocks = int(kv_bytes // (KV_TOKEN_BYTES_13B * block_size))
+        slots = blocks * block_size
+        watermark = -(-blocks // 100)
+        a, p, o = synth.serving_requests(seed, n, 160, 200, 1.0, reserve, None)
+        entry = {"workload": name, "kv_bytes": int(kv_bytes), "slots": slots, "block_size": block_size,
+                 "watermark_blocks": watermark, "max_batch": max_batch, "requests": n,
+                 "mean_prompt": round(float(p.mean()), 1), "mean_output": round(float(o.mean()), 1),
+                 "contiguous_reserve": reserve}
+        for kind in ("paged", "contiguous"):
+            t0 = time.perf_counter()
+            if kind == "paged":
+                trace, _ = sim.simulate_paged(blocks, block_size, watermark, max_batch, a, p, o, max_steps=1 << 21)
+            else:
+                trace, _ = sim.simulate_contiguous(slots, max_batch, a, p, o, np.full(n, reserve), max_steps=1 << 21)
+            dt = time.perf_counter() - t0
+            summary = sim.summarize(trace, slots)
+            summary = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in summary.items()}
+            summary["native_us_per_step"] = round(1e6 * dt / len(trace), 2)
+            entry[kind] = summary
+        configs.append(entry)
+    # the oracle beside the native simulator, on the first requests of the first budget
+    c = configs[0]
+    a, p, o = synth.serving_requests(seed, c["requests"], 160, 200, 1.0, reserve, None)
+    a, p, o = a[:oracle_requests], p[:oracle_requests], o[:oracle_requests]
+    args = (c["slots"] // block_size, block_size, c["watermark_blocks"], c["max_batch"], a, p, o)
+    t0 = time.perf_counter()
+    nat, _ = sim.simulate_paged(*args)
+    t_nat = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    rows, _ = ref.simulate_paged(*args)
+    t_ref = time.perf_counter() - t0
+    return {"metric": "continuous-batching memory simulator: useful share of held KV memory, paged vs contiguous "
+                      "reservation",
+            "data": "synthetic (seeded log-normal prompt/output lengths, all requests waiting at step 0)",
+            "configs": configs,
+            "oracle": {"sample": f"paged scheme, first {oracle_requests} requests of {c['workload']}",
+                       "steps": len(rows), "native_ms": round(1e3 * t_nat, 2), "oracle_ms": round(1e3 * t_ref, 1),
+                       "identical": bool(np.array_equal(nat, np.array(rows, dtype=np.int64)))}}
 
 
 def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=10):

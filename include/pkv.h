@@ -305,6 +305,58 @@ int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, con
                                     int32_t dtype, uint32_t flags, hipStream_t stream);
 
 /* ======================================================================
+ * Continuous-batching memory simulator (host only; the memory side of iteration-level
+ * scheduling, lesson note "Week 22 Day 2" section 4, under the paged and the contiguous
+ * scheme; slides 6, 7 and 15).
+ * ==================================================================== */
+
+/* Integers per trace row, in this order:
+ *   step, running, waiting        step index; requests in the batch and in the queue after
+ *                                 the step's admissions
+ *   used                          slots holding a real token (sum of the running lengths)
+ *   held, free, largest_free      slots given to running requests, slots not given, and the
+ *                                 most one request could take (paged: all free slots)
+ *   admitted, preempted, finished, decoded
+ *                                 requests admitted, evicted, finished and decoding this step
+ *   blocked_need                  slots the queue head asked for when admission stopped for
+ *                                 memory, else 0 (external fragmentation: free >= blocked_need
+ *                                 > largest_free)
+ *   final_sum                     sum of the running requests' final lengths P + O */
+#define PKV_SIM_FIELDS 13
+
+/* Requests (host arrays of n_requests): arrival step (>= 0, non-decreasing), prompt length P
+ * and output length O (both >= 1). A request holds P tokens after its prefill and P + O after
+ * its O-th decode step, when it finishes; a fresh request admitted at step t, never evicted,
+ * finishes at step t + O.
+ * One step: arrivals join the queue tail; every running request appends one token; finished
+ * requests are freed at once; the queue head is admitted while it fits and fewer than
+ * max_batch requests run (strict queue order); one trace row is written. The run ends after
+ * the step at which every request has finished.
+ * trace_out: host int64[max_steps * PKV_SIM_FIELDS], rows of the steps run (*n_steps_out of them);
+ * finish_out: host int64[n_requests], the step each request finished at.
+ * PKV_EINVAL for bad arguments, a request that can never fit, or a run longer than max_steps
+ * (outputs then unspecified). */
+
+/* Paged: a pool of num_blocks blocks of block_size slots (this library's allocator, fresh,
+ * ascending free order). A decode step appends one token to every running request in one
+ * all-or-nothing batch; if the pool is short, the newest running request is freed whole and
+ * returns to the queue head (slide 15), and the batch is tried again. An evicted request keeps
+ * its generated tokens and recomputes them: its next prefill writes P + (tokens generated).
+ * Admission needs ceil(tokens / block_size) + watermark_blocks free blocks. Every request must
+ * satisfy ceil((P + O) / block_size) + watermark_blocks <= num_blocks. */
+int pkv_sim_paged(int32_t num_blocks, int32_t block_size, int32_t watermark_blocks, int32_t max_batch,
+                  const int32_t *arrival, const int32_t *prompt_len, const int32_t *output_len, int32_t n_requests,
+                  int64_t max_steps, int64_t *trace_out, int64_t *n_steps_out, int64_t *finish_out);
+
+/* Contiguous: capacity slots in one linear range; admission reserves reserve_len[i] slots
+ * (P + O <= reserve_len[i] <= capacity; a system that does not know O reserves the maximum
+ * length, lesson note section 1) in the lowest-addressed free run that holds them (first fit),
+ * released on finish and merged with free neighbours. Nothing is evicted. */
+int pkv_sim_contiguous(int64_t capacity, int32_t max_batch, const int32_t *arrival, const int32_t *prompt_len,
+                       const int32_t *output_len, const int32_t *reserve_len, int32_t n_requests, int64_t max_steps,
+                       int64_t *trace_out, int64_t *n_steps_out, int64_t *finish_out);
+
+/* ======================================================================
  * Measurement companion (not part of the method).
  * ==================================================================== */
 

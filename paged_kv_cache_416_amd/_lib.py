@@ -43,6 +43,8 @@ SIGNATURES = {
     "pkv_prompt_digests": (ctypes.c_int, [_pi32, _i64, _i32, ctypes.POINTER(ctypes.c_uint8), _i64]),
     "pkv_seq_add_prompt": (ctypes.c_int, [_p, _i64, _pi32, _i32, _pi64, _pi32]),
     "pkv_pool_num_cached": (_i32, [_p]),
+    "pkv_sim_paged": (ctypes.c_int, [_i32, _i32, _i32, _i32, _pi32, _pi32, _pi32, _i32, _i64, _pi64, _pi64, _pi64]),
+    "pkv_sim_contiguous": (ctypes.c_int, [_i64, _i32, _pi32, _pi32, _pi32, _pi32, _i32, _i64, _pi64, _pi64, _pi64]),
     "pkv_reshape_and_cache": (ctypes.c_int, [_p, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32,
                                              _p]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i64, _i64, _pi32, _i32, _p]),

@@ -20,7 +20,7 @@ FLAGS = [
     "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["errors.cpp", "validate.cpp", "sha256.cpp", "pool.cpp", "cache_ops.hip", "attention.hip", "attention_gqa.hip", "prefill.hip", "probe.hip"]
+SOURCES = ["errors.cpp", "validate.cpp", "sha256.cpp", "pool.cpp", "sim.cpp", "cache_ops.hip", "attention.hip", "attention_gqa.hip", "prefill.hip", "probe.hip"]
 
 
 def _compile(src):
