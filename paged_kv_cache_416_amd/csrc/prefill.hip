@@ -4,24 +4,29 @@
 // slide 3: the prompt is processed in parallel; slides 9 and 10: keys and values are fetched
 // block by block through the block table).
 //
-// The grouped-query decode kernel's tile generalised: a wave owns 16 matrix rows, now (query
-// token, query head) pairs of one kv head (row r of a sequence and kv head is token r / G, head
-// kvh * G + r % G), and walks every 16-key tile up to its last row's position:
-//  * logits: S^T[key][row] = K[key][:] . Q^T[:][row] as 4 v_mfma_f32_16x16x32 over d;
-//  * weighted sum: O^T[d][row] = V^T[d][key] . P^T[key][row] as 8 v_mfma_f32_16x16x16 per
-//    16-bit part of the weights (each weight enters as a 16-bit part and the 16-bit rounding
-//    of its remainder), lane-local operands as in the decode kernel;
+// Matrix rows are (query token, query head) pairs of one kv head: row r of a sequence and kv
+// head is token r / G, head kvh * G + r % G. A workgroup owns W * RT * 16 consecutive rows (each
+// wave RT tiles of 16) and walks the keys up to its last row's position in steps of 32:
+//  * the step's keys and values (16 KiB, two 16-key tiles) are read once per workgroup, whole
+//    rows per load, through the block table, and written to a double-buffered LDS ring (rows
+//    padded to 272 bytes, so the operand reads below hit 16 distinct bank groups); one barrier
+//    per step;
+//  * logits: S^T[key][row] = K[key][:] . Q^T[:][row] as 4 v_mfma_f32_16x16x32 per 16-key tile;
+//  * weighted sum: O^T[d][row] = V^T[d][key] . P^T[key][row] as 8 v_mfma_f32_16x16x32 per
+//    16-bit part of the weights, the k slots 8g .. 8g+7 of lane group g taking keys 4g .. 4g+3 of
+//    the first tile and of the second, which is where the logits put them;
 //  * the causal mask is a per-lane compare of the key's position with row n's position.
-// Rows are independent, so the waves of a workgroup (consecutive row tiles, reading the same
-// key tiles through the caches) need no merge; a wave writes its rows and ends.
+// Rows are independent: a wave writes its rows and ends; the workgroups that need the most keys
+// (the last rows of each sequence) are dispatched first.
 #include "mfma.h"
 
 namespace pkv {
 namespace {
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillStages = 2;
-constexpr int kPrefillRowTiles = 2;  // 16-row tiles per wave, sharing each key/value tile it loads
+constexpr int kPrefillRowTiles = 2;  // 16-row tiles per wave
+constexpr int kStepKeys = 32;        // keys per step (two 16-key tiles)
+constexpr int kLdsRow = 272;         // bytes per staged row: 256 + 16 of padding
 
 struct PrefillParams {
     void *out;
@@ -32,14 +37,20 @@ struct PrefillParams {
     float scale_log2;
 };
 
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima: the global loads of later steps
+// stay in flight across the barrier)
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <class E, int B, int W, int RT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const PrefillParams p) {
     using M = Mfma<E>;
-    constexpr int D = 128, TR = 16, SPB = B / TR, ROWB = D * 2, NS = kPrefillStages;
-    static_assert(B % TR == 0, "block_size must be a multiple of 16");
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int D = 128, TR = 16, ROWB = D * 2, NT = W * 64, CPT = 2 * TR * 16 / NT;
+    static_assert(B % TR == 0 && CPT >= 1 && 2 * TR * 16 % NT == 0, "shape");
+    __shared__ __attribute__((aligned(16))) char lds[2][2][kStepKeys][kLdsRow];  // [buffer][K, V][key][byte]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int s = blockIdx.z, kvh = blockIdx.y;
     const int G = p.group;
@@ -49,8 +60,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int nq = __builtin_amdgcn_readfirstlane(p.query_start[s + 1]) - q0;
     const int ctx = clamp_ctx(__builtin_amdgcn_readfirstlane(p.ctx_lens[s]), p.ctx_cap);
     const int rows = nq * G;
-    const int row0 = (blockIdx.x * W + wave) * 16 * RT;  // the wave's RT row tiles start here
-    if (nq <= 0 || nq > ctx || row0 >= rows) return;  // uniform over the wave
+    const int wg_row0 = (gridDim.x - 1 - blockIdx.x) * W * RT * 16;
+    if (nq <= 0 || nq > ctx || wg_row0 >= rows) return;  // uniform over the workgroup
+    const int row0 = wg_row0 + wave * RT * 16;  // a wave past the last row still loads and waits
 
     // row n of each of the wave's row tiles: query token, head, position
     bool row_ok[RT];
@@ -63,10 +75,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         head[rt] = kvh * G + (row_ok[rt] ? r % G : 0);
         qpos[rt] = ctx - nq + tok[rt];
     }
-    const int last_tok = (min(row0 + 16 * RT - 1, rows - 1)) / G;
-    // keys these rows need: [0, kend) (uniform: it sizes the loop and the buffer resources)
-    const int kend = __builtin_amdgcn_readfirstlane(ctx - nq + last_tok + 1);
-    const int ntile = (kend + TR - 1) / TR;
+    // keys the workgroup needs: [0, kend); keys this wave's rows need: [0, kend_w)
+    const int kend = __builtin_amdgcn_readfirstlane(ctx - nq + min(wg_row0 + W * RT * 16 - 1, rows - 1) / G + 1);
+    const int kend_w = row0 < rows ? ctx - nq + min(row0 + RT * 16 - 1, rows - 1) / G + 1 : 0;
+    const int nstep = (kend + kStepKeys - 1) / kStepKeys;
 
     u32x4 qv[RT][4];
 #pragma unroll
@@ -81,30 +93,46 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     TableEntry *trow = (TableEntry *)(p.tables + static_cast<int64_t>(s) * p.max_blocks);  // address-space cast
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
-    const unsigned koff = n * ROWB + g * 16;      // + kk * 64: row n, chunk 4*kk + g
-    const unsigned voff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n
 
+    // global loads of one step: thread chunk c = tid + k * NT is row c / 16 (its 16-key tile u =
+    // row / 16, uniform over a wave), 16-byte column c % 16
     struct Stage {
-        u32x4 k[4], v[4];
-        int t;    // key tile (>= ntile: a stand-in)
-        bool ok;  // table entry inside the pool
+        u32x4 k[CPT], v[CPT];
+        int t;        // step (>= nstep: a stand-in)
+        bool ok[2];   // table entries inside the pool
     };
-    int ct = 0;  // next tile to issue; its table entry is looked up one tile ahead
-    int cpb = trow[0];
+    int ct = 0;  // next step to issue; its table entries are looked up one step ahead
+    int cp[2] = {trow[0], trow[min(TR, kend - 1) / B]};
     auto issue = [&](Stage &S) {
         S.t = ct;
-        const int jt = min(ct, ntile - 1);
-        S.ok = static_cast<uint32_t>(cpb) < p.num_blocks;
-        const int64_t blk = S.ok ? cpb : 0;
-        const int64_t tile = ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
-        const int keys = ct < ntile && S.ok ? min(TR, kend - ct * TR) : 0;
-        const auto kr_ = tile_rsrc(kc + tile, keys * ROWB), vr_ = tile_rsrc(vc + tile, keys * ROWB);
+        int64_t tile[2];
+        int bytes[2];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) S.k[kk] = kv_buffer_load<false>(kr_, koff + kk * 64);
+        for (int u = 0; u < 2; ++u) {
+            const int kb = ct * kStepKeys + u * TR;
+            S.ok[u] = static_cast<uint32_t>(cp[u]) < p.num_blocks;
+            const int64_t blk = S.ok[u] ? cp[u] : 0;
+            tile[u] = ((blk * p.num_kv_heads + kvh) * B + kb % B) * ROWB;
+            // uniform, but the clamp is done with a vector instruction: readfirstlane keeps the
+            // descriptor scalar
+            bytes[u] = __builtin_amdgcn_readfirstlane((ct < nstep && S.ok[u] ? max(0, min(TR, kend - kb)) : 0) * ROWB);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S.v[i] = kv_buffer_load<false>(vr_, voff + i * ROWB);
+        for (int k = 0; k < CPT; ++k) {
+            // the chunk's 16-key tile: known at compile time up to 256 threads, else the wave's
+            // half of the workgroup; the scalar inputs are selected, not the descriptors (a
+            // select of descriptors is done per lane and would loop over the lanes at each load)
+            const int u = NT <= 256 ? (k * NT) >> 8 : wave >> 2;
+            const int c = tid + k * NT;
+            const unsigned off = ((c >> 4) & 15) * ROWB + (c & 15) * 16;
+            const int64_t tu = u ? tile[1] : tile[0];
+            const int bu = u ? bytes[1] : bytes[0];
+            S.k[k] = kv_buffer_load<false>(tile_rsrc(kc + tu, bu), off);
+            S.v[k] = kv_buffer_load<false>(tile_rsrc(vc + tu, bu), off);
+        }
         ++ct;
-        cpb = trow[min(ct, ntile - 1) / SPB];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) cp[u] = trow[min(ct * kStepKeys + u * TR, kend - 1) / B];
     };
 
     float m[RT], lsum[RT];
@@ -117,21 +145,39 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int j = 0; j < 8; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // one key tile against every row tile of the wave (the tile's loads serve RT * 16 rows)
-    auto consume = [&](Stage &S) {
+    // the staged step in buffer b against every row tile of the wave
+    auto consume = [&](int b, int t, const bool ok[2]) {
+        f32x4 c[RT][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 kf[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                kf[kk] = *reinterpret_cast<const u32x4 *>(&lds[b][0][u * TR + n][(4 * kk + g) * 16]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                c[rt][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) c[rt][u] = M::mma(kf[kk], qv[rt][kk], c[rt][u]);
+            }
+        }
+        u32x4 vf[2][4];  // rows u * 16 + 4g + i, 16-byte column n
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vf[u][i] = *reinterpret_cast<const u32x4 *>(&lds[b][1][u * TR + 4 * g + i][n * 16]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            float sc[2][4], mloc = -INFINITY;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[kk], qv[rt][kk], c);
-            float sc[4], mloc = -INFINITY;
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kpos = S.t * TR + 4 * g + i;  // a stand-in's keys all lie past kend
-                const bool valid = S.ok && kpos <= qpos[rt] && kpos < kend;
-                sc[i] = valid ? c[i] * p.scale_log2 : -INFINITY;
-                mloc = fmaxf(mloc, sc[i]);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int kpos = t * kStepKeys + u * TR + 4 * g + i;  // qpos < kend: kend is implied
+                    sc[u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
+                    mloc = fmaxf(mloc, sc[u][i]);
+                }
             mloc = max_over_lane_groups(mloc);
             const float m_new = fmaxf(m[rt], mloc);
             const float m_ref = m_new == -INFINITY ? 0.f : m_new;
@@ -141,42 +187,70 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[rt][j] *= alpha;
             }
-            const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
-            const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
-            const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
-            const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
-            const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
-            lsum[rt] = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum[rt]))));
-            const u32x2 ph = {h01, h23}, pr = {r01, r23};
+            unsigned h[4], r[4];  // weights of keys (u, 2w), (u, 2w + 1) in word 2u + w
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const float e0 = fast_exp2(sc[u][2 * w] - m_ref), e1 = fast_exp2(sc[u][2 * w + 1] - m_ref);
+                    const unsigned hw = M::pack2(e0, e1);
+                    h[2 * u + w] = hw;
+                    r[2 * u + w] = M::pack2(e0 - M::value(hw & 0xffffu), e1 - M::value(hw >> 16));
+                }
+            float l = lsum[rt];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l = M::sum2(h[w], l);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) l = M::sum2(r[w], l);
+            lsum[rt] = l;
+            const u32x4 ph = {h[0], h[1], h[2], h[3]}, pr = {r[0], r[1], r[2], r[3]};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int w = j >> 1;
                 const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[1], w), word(S.v[0], w), sel),
-                                  __builtin_amdgcn_perm(word(S.v[3], w), word(S.v[2], w), sel)};
-                acc[rt][j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[rt][j]));
+                const u32x4 vt = {__builtin_amdgcn_perm(word(vf[0][1], w), word(vf[0][0], w), sel),
+                                  __builtin_amdgcn_perm(word(vf[0][3], w), word(vf[0][2], w), sel),
+                                  __builtin_amdgcn_perm(word(vf[1][1], w), word(vf[1][0], w), sel),
+                                  __builtin_amdgcn_perm(word(vf[1][3], w), word(vf[1][2], w), sel)};
+                acc[rt][j] = M::mma(vt, pr, M::mma(vt, ph, acc[rt][j]));
             }
             m[rt] = m_new;
         }
     };
 
-    // ring of NS stages over the wave's key tiles; whole rounds, the end tested at a round's
-    // start (straight-line rounds keep the wait counts exact; the last may consume stand-ins)
-    Stage R[NS];
-    __builtin_amdgcn_sched_barrier(0);
+    // one step: stage the loaded rows in LDS, reuse the registers for the step two ahead, wait
+    // for every wave's rows, compute (a wave whose rows need none of these keys skips it)
+    auto step = [&](Stage &S, int b) {
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) {
-        issue(R[i]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (;;) {
-        if (R[0].t >= ntile) break;
-#pragma unroll
-        for (int rr = 0; rr < NS; ++rr) {
-            issue(R[(rr + NS - 1) % NS]);
-            consume(R[rr]);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int k = 0; k < CPT; ++k) {
+            const int c = tid + k * NT;
+            *reinterpret_cast<u32x4 *>(&lds[b][0][c >> 4][(c & 15) * 16]) = S.k[k];
+            *reinterpret_cast<u32x4 *>(&lds[b][1][c >> 4][(c & 15) * 16]) = S.v[k];
         }
+        const int t = S.t;
+        const bool ok[2] = {S.ok[0], S.ok[1]};
+        issue(S);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (t * kStepKeys < kend_w) consume(b, t, ok);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // two register stages in a ring; whole rounds, the end tested at a round's start (straight-
+    // line rounds keep the wait counts exact; the last may be a stand-in step). Every wave runs
+    // the same number of steps, so the barriers match.
+    Stage R[2];
+    __builtin_amdgcn_sched_barrier(0);
+    issue(R[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(R[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (;;) {
+        if (R[0].t >= nstep) break;
+        step(R[0], 0);
+        step(R[1], 1);
     }
 
     // each row's weight sum over the four lane groups; lane (n, g) holds d = 8 (4g + i) + j
@@ -201,8 +275,9 @@ int launch(const PrefillParams &p, int32_t max_query_len, int32_t num_seqs, hipS
     const int64_t tiles = ceil_div(static_cast<int64_t>(max_query_len) * p.group, 16);
     const int64_t gx = ceil_div(tiles, kPrefillWaves * kPrefillRowTiles);
     if (gx > INT32_MAX) return fail(PKV_EINVAL, "pkv_paged_attention_prefill: max_query_len too large");
-    hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles>), dim3(static_cast<unsigned>(gx), p.num_kv_heads, num_seqs),
-                       dim3(kPrefillWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles>),
+                       dim3(static_cast<unsigned>(gx), p.num_kv_heads, num_seqs), dim3(kPrefillWaves * 64), 0, stream,
+                       p);
     return hip_status(hipGetLastError(), "pkv_paged_attention_prefill launch");
 }
 
