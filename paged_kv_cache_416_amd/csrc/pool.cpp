@@ -67,6 +67,7 @@ struct pkv_pool {
     struct Seq {
         std::vector<int32_t> blocks;  // logical block j -> physical block
         int64_t len = 0;              // tokens written
+        uint64_t stamp = 0;           // the last batched append that named it
     };
     int32_t num_blocks = 0;
     int32_t block_size = 0;
@@ -78,6 +79,11 @@ struct pkv_pool {
     std::vector<char> has_digest;
     std::unordered_map<Digest, int32_t, DigestHash> by_digest;
     std::unordered_map<int64_t, Seq> seqs;
+    // batched-append scratch, kept between calls so that a decode step allocates nothing
+    uint64_t append_stamp = 0;
+    std::vector<Seq *> batch;
+    std::vector<int32_t> pending_drop;  // per block: shared last blocks given up earlier in the batch
+    std::vector<int32_t> touched;       // blocks whose pending_drop is non-zero
 
     int64_t available() const { return static_cast<int64_t>(free_stack.size() + cached_free.size()); }
 
@@ -219,37 +225,57 @@ int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_toke
         return fail(PKV_EINVAL, "pkv_seq_append: bad arguments");
     const int64_t B = pool->block_size;
     // Validation and a dry run that counts the blocks the whole batch needs, so that a
-    // batch the pool cannot serve changes nothing (slide 15: all or nothing).
-    std::unordered_set<int64_t> seen;
-    std::unordered_map<int32_t, int32_t> pending_drop;  // shared last blocks given up earlier in this batch
+    // batch the pool cannot serve changes nothing (slide 15: all or nothing). A sequence named
+    // twice is caught by its stamp; pending_drop counts, per block, the sharers that already
+    // gave up a shared partial last block earlier in the batch (cleared again on every exit).
+    const uint64_t stamp = ++pool->append_stamp;
+    if (pool->pending_drop.size() != static_cast<size_t>(pool->num_blocks)) pool->pending_drop.assign(pool->num_blocks, 0);
+    auto &pending = pool->pending_drop;
+    auto &touched = pool->touched;
+    auto clear_pending = [&]() {
+        for (const int32_t b : touched) pending[b] = 0;
+        touched.clear();
+    };
     int64_t need = 0, total_tokens = 0;
     int32_t pairs = 0;
-    std::vector<pkv_pool::Seq *> seqv(n_seqs);
+    auto &seqv = pool->batch;
+    seqv.resize(n_seqs);
     for (int32_t i = 0; i < n_seqs; ++i) {
         auto it = pool->seqs.find(seq_ids[i]);
-        if (it == pool->seqs.end())
+        if (it == pool->seqs.end()) {
+            clear_pending();
             return fail(PKV_ENOSEQ, "pkv_seq_append: unknown sequence %lld", (long long)seq_ids[i]);
-        if (!seen.insert(seq_ids[i]).second)
-            return fail(PKV_EINVAL, "pkv_seq_append: sequence %lld appears twice", (long long)seq_ids[i]);
-        if (n_tokens[i] < 0) return fail(PKV_EINVAL, "pkv_seq_append: n_tokens[%d] = %d < 0", i, n_tokens[i]);
+        }
         pkv_pool::Seq &q = it->second;
+        if (q.stamp == stamp) {
+            clear_pending();
+            return fail(PKV_EINVAL, "pkv_seq_append: sequence %lld appears twice", (long long)seq_ids[i]);
+        }
+        q.stamp = stamp;
+        if (n_tokens[i] < 0) {
+            clear_pending();
+            return fail(PKV_EINVAL, "pkv_seq_append: n_tokens[%d] = %d < 0", i, n_tokens[i]);
+        }
         seqv[i] = &q;
         const int64_t n = n_tokens[i];
         if (n == 0) continue;
         if (q.len % B) {
-            int32_t last = q.blocks.back();
-            if (pool->ref[last] - pending_drop[last] > 1) {
-                ++pending_drop[last];
+            const int32_t last = q.blocks.back();
+            if (pool->ref[last] - pending[last] > 1) {
+                if (pending[last]++ == 0) touched.push_back(last);
                 ++need;
                 ++pairs;
             }
         }
         const int64_t blocks_after = pkv::ceil_div(q.len + n, B);
-        if (blocks_after > INT32_MAX)
+        if (blocks_after > INT32_MAX) {
+            clear_pending();
             return fail(PKV_EINVAL, "pkv_seq_append: sequence %lld too long", (long long)seq_ids[i]);
+        }
         need += blocks_after - static_cast<int64_t>(q.blocks.size());
         total_tokens += n;
     }
+    clear_pending();
     if (total_tokens > 0 && !slots_out) return fail(PKV_EINVAL, "pkv_seq_append: slots_out is NULL");
     if (pairs > max_pairs)
         return fail(PKV_EINVAL, "pkv_seq_append: %d copy-on-write pairs, room for %d", pairs, max_pairs);
