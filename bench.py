@@ -43,7 +43,7 @@ COUNTERS = {
                    "attn_decode_kernel", 0, 0),
     "8b-gqa-prefix": ("attn_gqa_bf16_8b_balanced_counters.txt",
                       [CSRC + "attention_gqa.hip", CSRC + "mfma.h", CSRC + "attention.h", CSRC + "common.h"],
-                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, FLAG_CACHED_KV),
+                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, 0),
 }
 
 

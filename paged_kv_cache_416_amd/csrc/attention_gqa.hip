@@ -9,10 +9,16 @@
 //
 // Work unit: a tile of 16 consecutive rows (tokens) of one (block, kv head). With lane l,
 // g = l / 16, n = l % 16:
+//  * K and V are loaded alike, as whole rows: load i brings lane l chunk n of row 4g + i, so one
+//    load instruction covers four whole 256-byte rows and every 128-byte line is fetched by one
+//    instruction (which lets the loads be non-temporal without fetching a line twice);
 //  * logits: S^T[token][head] = K[token][:] . Q^T[:][head] as 4 v_mfma_f32_16x16x32 over d.
 //    Lane l supplies K row n, 16-byte chunk 4*kk + g (the A operand) and query head n, the same
 //    chunk (the B operand; heads >= G are zero), and receives the logits of head n for tokens
-//    4g .. 4g+3 of the tile;
+//    4g .. 4g+3 of the tile. The K tile reaches that operand layout through a 4 KiB LDS tile
+//    private to the wave: written as loaded, read back per operand, with chunk c of row r stored
+//    at position c ^ r of the row, so that neither the 16 lanes writing one row nor the 16 lanes
+//    reading one chunk of 16 rows meet in a bank;
 //  * weighted sum: O^T[d][head] = V^T[d][token] . P^T[token][head] as 8 v_mfma_f32_16x16x16,
 //    MFMA j covering d = 8m + j (m = 0..15). Lane l's P^T operand is its own 4 softmax
 //    weights (head n, tokens 4g .. 4g+3) and its V^T operand is element j of its own 4 V loads
@@ -43,6 +49,7 @@ template <int W>
 struct GqaLds {
     float m[W][kMaxGroup], l[W][kMaxGroup];
     float acc[W][kMaxGroup][128];
+    u32x4 kt[W][16 * 16];  // each wave's K tile, 16 rows x 16 chunks, chunk positions swizzled by row
 };
 
 
@@ -103,7 +110,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     lookup();
 
     struct Stage {
-        u32x4 k[U][4], v[U][4];
+        u32x4 k[U][4], v[U][4];  // [i]: chunk n of row 4g + i
         int st;      // stage index within the range (>= nstage: a stand-in)
         bool ok[U];  // table entry inside the pool
     };
@@ -111,8 +118,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     // Every load is unconditional (exact wait counts) and goes through a buffer resource that
     // ends at the tile's last row inside [t0, t1): rows past it, a stand-in tile and a tile whose
     // table entry is rejected read as zeros, with no memory traffic; consume() masks them out.
-    const unsigned koff = n * ROWB + g * 16;      // + kk * 64: row n, chunk 4*kk + g
-    const unsigned voff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n
+    const unsigned roff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n (K and V)
     auto issue = [&](Stage &S) {
         S.st = cst;
 #pragma unroll
@@ -131,9 +137,9 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
             const int rows = k < ntile && S.ok[u] ? min(TR, t1 - (jt0 + k) * TR) : 0;
             const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) S.k[u][kk] = kv_buffer_load<NT>(kr_, koff + kk * 64);
+            for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<NT>(kr_, roff + i * ROWB);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<NT>(vr_, voff + i * ROWB);
+            for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<NT>(vr_, roff + i * ROWB);
         }
         cst += W;
         lookup();
@@ -144,14 +150,29 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // The K tile in the A-operand layout: through the wave's LDS tile (a wave's LDS operations
+    // complete in order, so a tile's reads see its writes and the next tile's writes follow them).
+    u32x4 *kt = lds.kt[wave];
+    auto k_operand = [&](const u32x4 (&rows)[4], u32x4 (&ka)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            kt[r * 16 + (n ^ r)] = rows[i];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = kt[n * 16 + ((4 * kk + g) ^ n)];
+    };
+
     auto consume = [&](Stage &S) {
         float sc[U][4];
         float mloc = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            u32x4 ka[4];
+            k_operand(S.k[u], ka);
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) c = M::mma(S.k[u][kk], qv[kk], c);
+            for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
             const int tok0 = (jt0 + S.st * U + u) * TR;  // a stand-in's rows all lie past t1
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
