@@ -36,14 +36,14 @@ FLAG_CACHED_KV = 2  # the library's cached K/V load flag
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "paged_kv_cache_416_amd/csrc/"
 # workload -> (counter summary under profiles/, sources of its attention kernel, kernel name part,
-#              partition size and flags the summary was taken at)
+#              partition size, flags and cached-load hint the summary was taken at)
 COUNTERS = {
     "13b-decode": ("attn_decode_f16_13b_counters.txt",
                    [CSRC + "attention.hip", CSRC + "attention.h", CSRC + "common.h"],
-                   "attn_decode_kernel", 0, 0),
+                   "attn_decode_kernel", 0, 0, "none"),
     "8b-gqa-prefix": ("attn_gqa_bf16_8b_balanced_counters.txt",
                       [CSRC + "attention_gqa.hip", CSRC + "mfma.h", CSRC + "attention.h", CSRC + "common.h"],
-                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, 0),
+                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, 0, "shared"),
 }
 
 
@@ -99,6 +99,8 @@ def parse():
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
+    ap.add_argument("--cached-lens", choices=["default", "none", "shared"], default="default",
+                    help="cached-load hint: none, or each sequence's shared prefix from the reference counts")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain elementwise kernel over this many MiB (counter calibration)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "CMD"))
@@ -119,9 +121,10 @@ def make_workload(name):
     if name.startswith("sweep-b"):
         return synth.block_sweep(block_size=int(name[7:])), 0, 0
     if name == "gqa":
-        # every sequence maps the same 1024-token prefix blocks: the scheduler, which built the
-        # tables from reference counts, asks for cached K/V loads
-        return synth.gqa_shared_prefix(), 512, FLAG_CACHED_KV
+        # every sequence maps the same 1024-token prefix blocks; the reference counts give each
+        # sequence's shared prefix, which is loaded through the caches (the default cached-load
+        # hint of this workload), the private blocks non-temporally
+        return synth.gqa_shared_prefix(), 512, 0
     raise ValueError(name)
 
 
@@ -163,11 +166,12 @@ def timed_launches(fn, n, stream):
     return 1e3 * a.elapsed_time(b) / n
 
 
-def read_counters(workload, P, flags):
+def read_counters(workload, P, flags, hint):
     """Measured HBM bytes per attention launch from the committed counter summary, if it was
-    taken at this partition size and flags on the kernel source as it is now; else None."""
+    taken at this partition size, flags and cached-load hint on the kernel source as it is now;
+    else None."""
     entry = COUNTERS.get(workload)
-    if entry is None or (P, flags) != (entry[3], entry[4]):
+    if entry is None or (P, flags, hint) != (entry[3], entry[4], entry[5]):
         return None
     path = os.path.join(PROFILES, entry[0])
     if not os.path.exists(path):
@@ -210,6 +214,7 @@ def main():
     torch.cuda.set_device(dev)
     w, default_P, default_flags = make_workload(args.workload)
     flags = default_flags if args.flags < 0 else args.flags
+    hint = args.cached_lens if args.cached_lens != "default" else ("shared" if args.workload == "gqa" else "none")
     P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
     if P is None:
         P = int(args.partition)
@@ -229,6 +234,7 @@ def main():
     tb = torch.from_numpy(tb_host).to(dev)
     ctx_dev = torch.from_numpy(ctx_host).to(dev)
     max_ctx = int(ctx_host.max())
+    cached_lens = cache.shared_prefix_lens(w.batch) if hint == "shared" else None
     ctx = w.final_lengths()
     q = to_device(w.q, dt, dev)
     out = torch.empty_like(q)
@@ -243,7 +249,7 @@ def main():
 
     def attend(i):
         r = i % args.replicas
-        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, flags)
+        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, flags, cached_lens)
 
     def one_step(i):
         r = i % args.replicas
@@ -266,7 +272,7 @@ def main():
 
     value = (unique_b + w_bytes) / (ms_per_step * 1e-3) / 1e9
     achieved = unique_b / (attn_us * 1e-6) / 1e9
-    traffic = read_counters(w.name, P, flags)
+    traffic = read_counters(w.name, P, flags, hint)
 
     result = {
         "metric": METRIC,
@@ -283,7 +289,7 @@ def main():
         "data": "synthetic (seeded N(0,1)*0.5 keys/values, seeded context lengths and physical block order)",
         "config": {"workload": w.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": B, "sum_context": int(ctx.sum()), "max_context": int(ctx.max()),
-                   "partition_size": P, "flags": flags, "replicas": args.replicas},
+                   "partition_size": P, "flags": flags, "cached_lens": hint, "replicas": args.replicas},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "decode_tokens_per_s_attention_only": {
@@ -646,7 +652,7 @@ def summarize_counters(workload, fetch_csv, write_csv, out, cmd_fetch, cmd_write
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     probe = [k for k in fetch if "neg_kernel" in k]
-    _, sources, kname, _, _ = COUNTERS[workload]
+    _, sources, kname, _, _, _ = COUNTERS[workload]
     attn = [k for k in fetch if kname in k]
     if len(probe) != 1 or len(attn) != 1:
         raise SystemExit(f"expected one probe and one attention kernel, got {probe} / {attn}")

@@ -176,6 +176,13 @@ int pkv_seq_migrate(pkv_pool *src, pkv_pool *dst, const int64_t *seq_ids, int32_
 int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t max_blocks,
                            int32_t pad_value, int32_t *tables_out, int32_t *ctx_out);
 
+/* Shared prefix of n sequences, from the reference counts (lesson note section 3.1: sharing a
+ * block increments its count; slide 14: sequences share blocks): out[i] (host) = the tokens of
+ * seq_ids[i] that lie in its leading blocks with a count above one, i.e.
+ * min(length, block_size * j) for the first j blocks of its table that are all shared. The
+ * cached_lens hint of pkv_paged_attention_decode. An unknown sequence: PKV_ENOSEQ, out unchanged. */
+int pkv_shared_prefix_lens(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t *out);
+
 /* ======================================================================
  * Device kernels. dtype is a pkv_dtype; all tensors of one call share it.
  * ==================================================================== */
@@ -252,6 +259,15 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *  workspace:     device, >= pkv_decode_workspace_bytes(...) bytes, 16-byte aligned;
  *                 may be NULL when partition_size == 0.
  *  flags:         PKV_FLAG_SCALAR_GQA and/or PKV_FLAG_CACHED_KV, or 0; other bits are PKV_EINVAL.
+ *  cached_lens:   NULL, or device int32[num_seqs]: a load-policy hint. The first cached_lens[s]
+ *                 tokens of sequence s sit in blocks other sequences of the batch also read (a
+ *                 shared prefix; slide 14 and lesson note section 3.1: sharing is tracked by
+ *                 reference counts, e.g. pkv_shared_prefix_lens). Their K/V loads go through
+ *                 the caches, so the re-reads hit L2 instead of HBM; the other tokens are
+ *                 loaded non-temporally. Any value is allowed (negative: none; past the length:
+ *                 all). Not read with PKV_FLAG_CACHED_KV, which sends every load through the
+ *                 caches. Neither changes any arithmetic: results are bit-identical with or
+ *                 without them.
  * Device-side guards (never faults on bad tables, but the result is then unspecified):
  * lengths are clamped to [0, min(max_context_len, max_blocks_per_seq*block_size)] and a
  * table entry outside [0, num_blocks) contributes no tokens.
@@ -267,7 +283,7 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
                                const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                               int32_t dtype, uint32_t flags, hipStream_t stream);
+                               int32_t dtype, uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
 
 /* Prefill (chunked) attention over the paged cache: the last n_s = query_start[s+1] -
  * query_start[s] tokens of each sequence s are queries, and query i of s, at position

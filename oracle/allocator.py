@@ -248,6 +248,15 @@ class BlockPool:
             self.free_seq(s)
         return [(b, moved_to[b]) for b in first_use]
 
+    def shared_prefix_len(self, sid):
+        """Tokens of sid in the leading run of its blocks whose reference count is above one
+        (blocks other sequences also hold; lesson note section 3.1, slide 14)."""
+        blocks, n = self.seqs[sid]
+        j = 0
+        while j < len(blocks) and self.ref[blocks[j]] > 1:
+            j += 1
+        return min(n, j * self.block_size)
+
     def tables(self, sids, max_blocks, pad=-1):
         rows, ctx = [], []
         for s in sids:

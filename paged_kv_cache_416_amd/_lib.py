@@ -39,6 +39,7 @@ SIGNATURES = {
     "pkv_seq_blocks": (_i32, [_p, _i64, _pi32, _i32]),
     "pkv_seq_append": (ctypes.c_int, [_p, _pi64, _pi32, _i32, _pi64, _pi32, _i32, _pi32]),
     "pkv_build_block_tables": (ctypes.c_int, [_p, _pi64, _i32, _i32, _i32, _pi32, _pi32]),
+    "pkv_shared_prefix_lens": (ctypes.c_int, [_p, _pi64, _i32, _pi32]),
     "pkv_seq_migrate": (ctypes.c_int, [_p, _p, _pi64, _i32, _pi32, _i32, _pi32]),
     "pkv_prompt_digests": (ctypes.c_int, [_pi32, _i64, _i32, ctypes.POINTER(ctypes.c_uint8), _i64]),
     "pkv_seq_add_prompt": (ctypes.c_int, [_p, _i64, _pi32, _i32, _pi64, _pi32]),
@@ -52,7 +53,7 @@ SIGNATURES = {
                                        _p]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "pkv_paged_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
-                                                  _i32, _f32, _i32, _p, _sz, _i32, _u32, _p]),
+                                                  _i32, _f32, _i32, _p, _sz, _i32, _u32, _p, _p]),
     "pkv_contiguous_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                                        _f32, _i32, _p, _sz, _i32, _u32, _p]),
     "pkv_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),

@@ -83,11 +83,19 @@ class PagedKVCache:
                 int(ctx.max(initial=0)))
 
     # -- device side ----------------------------------------------------
-    def attention(self, q, sids, scale, partition_size=0, flags=0, out=None):
+    def shared_prefix_lens(self, sids):
+        """Device int32 [n]: tokens of each sequence in its leading shared blocks (the cached-load hint)."""
+        return torch.from_numpy(self.pool.shared_prefix_lens(sids)).to(self.device)
+
+    def attention(self, q, sids, scale, partition_size=0, flags=0, out=None, cached_lens=None):
+        """cached_lens: None, "shared" (from the pool's reference counts) or a device int32 [n]."""
         tb, ctx, mx = self.tables(sids)
         out = torch.empty_like(q) if out is None else out
         ws = kernels.alloc_workspace(q.shape[0], q.shape[1], q.shape[2], mx, partition_size, self.device)
-        return kernels.paged_attention_decode(out, q, self.k, self.v, tb, ctx, mx, scale, partition_size, ws, flags)
+        if isinstance(cached_lens, str):
+            cached_lens = self.shared_prefix_lens(sids)
+        return kernels.paged_attention_decode(out, q, self.k, self.v, tb, ctx, mx, scale, partition_size, ws, flags,
+                                              cached_lens)
 
 
 def to_device(a: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:

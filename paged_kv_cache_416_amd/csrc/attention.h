@@ -89,6 +89,7 @@ struct AttnParams {
     const void *v;
     const int32_t *tables;
     const int32_t *ctx_lens;
+    const int32_t *cached_lens;  // kLoadSplit: per sequence, tokens [0, n) are loaded through the caches
     float *ws;             // split workspace: acc [S*Hq*P][D], then m [S*Hq*P], then l [S*Hq*P]
     int64_t ws_rows;       // S * Hq * num_parts
     uint32_t num_blocks;   // paged: pool size (< 2^31)
@@ -302,9 +303,14 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, uint32_t by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, static_cast<int>(bytes), kRawBufferConfig);
 }
 
-// K/V loads. NT (the default): non-temporal, for blocks read once per call; otherwise through
-// the caches, for blocks several sequences of the batch read (a shared prefix), whose re-reads
-// then hit the L2 or the last-level cache instead of HBM.
+// How a kernel loads K/V: non-temporal, for blocks read once per call; through the caches, for
+// blocks several sequences of the batch read (a shared prefix), whose re-reads then hit the L2
+// or the last-level cache instead of HBM; or split per sequence: its first cached_lens[s]
+// tokens through the caches (the blocks it shares), the rest non-temporal. The policy changes
+// no arithmetic.
+enum LoadPolicy { kLoadStream = 0, kLoadCached = 1, kLoadSplit = 2 };
+
+// K/V loads. NT: non-temporal; otherwise through the caches.
 template <bool NT>
 __device__ inline u32x4 kv_load(const char *p) {
     if constexpr (NT) return nt_load(p);
@@ -322,7 +328,7 @@ __device__ inline u32x4 kv_buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // MFMA grouped-query kernel (attention_gqa.hip). gqa_mfma_supported tells whether a shape has
 // an MFMA build; launch_gqa_mfma enqueues it (and the reduce pass in split mode).
 bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
-int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, bool cached,
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int load_policy,
                     int32_t num_seqs, int32_t grid_parts, hipStream_t stream);
 // The partition merge (attention.hip), shared by both kernels.
 int launch_reduce(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t num_seqs, hipStream_t stream);

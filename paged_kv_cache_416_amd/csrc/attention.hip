@@ -68,7 +68,7 @@ struct MhaLds {
 // Tokens [t0, t1) of sequence s for query head h (t0 a multiple of the tile rows, t0 < t1 <= the
 // length): the workgroup's merged result goes to sink. Uniform over the workgroup; ends with a
 // barrier, so the caller may run it again on the same LDS.
-template <class E, int D, int B, bool PAGED, int W, bool NT>
+template <class E, int D, int B, bool PAGED, int W, int POL>
 __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int t1, const Sink &sink,
                                  MhaLds<W, D> &lds) {
     using SH = Shape<E, D, B>;
@@ -94,6 +94,8 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
         return j < p.max_blocks ? trow[j] : 0;
     };
     if constexpr (PAGED) tb = fetch_table(0);
+    // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)
+    const int clen = POL == kLoadSplit ? __builtin_amdgcn_readfirstlane(p.cached_lens[s]) : 0;
     const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
 
     const char *kc = static_cast<const char *>(p.k);
@@ -137,12 +139,24 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
             const char *kt = kc + tile, *vt = vc + tile;  // uniform: a scalar base for the loads
             S.tok0[u] = (jt0 + wave + k * W) * TR;
             const int lim = t1 - 1 - S.tok0[u];  // last row inside the context
+            unsigned off[NL];
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 const unsigned row = clamp ? min(l * RPI + r0, lim) : l * RPI + r0;
-                const unsigned off = row * (D * E::ELT) + c * (VEC * E::ELT);
-                S.k[u][l] = kv_load<NT>(kt + off);
-                S.v[u][l] = kv_load<NT>(vt + off);
+                off[l] = row * (D * E::ELT) + c * (VEC * E::ELT);
+            }
+            if (POL == kLoadCached || (POL == kLoadSplit && S.tok0[u] < clen)) {
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    S.k[u][l] = kv_load<false>(kt + off[l]);
+                    S.v[u][l] = kv_load<false>(vt + off[l]);
+                }
+            } else {
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    S.k[u][l] = kv_load<true>(kt + off[l]);
+                    S.v[u][l] = kv_load<true>(vt + off[l]);
+                }
             }
         }
     };
@@ -276,7 +290,7 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
 
 // Per-item schedule: grid = (parts, num_q_heads, num_seqs), block = 64 * W; one workgroup per
 // (sequence, query head[, partition]).
-template <class E, int D, int B, bool PAGED, int W, bool NT>
+template <class E, int D, int B, bool PAGED, int W, int POL>
 __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
     __shared__ MhaLds<W, D> lds;
     const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
@@ -294,12 +308,12 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         const int64_t wr = row_q * p.num_parts + part;
         sink = Sink{p.ws + wr * D, p.ws + p.ws_rows * D + wr, p.ws + p.ws_rows * (D + 1) + wr, 0, 0};
     }
-    mha_range<E, D, B, PAGED, W, NT>(p, s, h, t0, t1, sink, lds);
+    mha_range<E, D, B, PAGED, W, POL>(p, s, h, t0, t1, sink, lds);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
 // (work rows = (sequence, query head)); cut rows are merged by attn_reduce_balanced_kernel.
-template <class E, int D, int B, bool PAGED, int W, bool NT>
+template <class E, int D, int B, bool PAGED, int W, int POL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_balanced_kernel(
     const AttnParams p) {
     __shared__ MhaLds<W, D> lds;
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_walk<D, false>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        mha_range<E, D, B, PAGED, W, NT>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
+        mha_range<E, D, B, PAGED, W, POL>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
     });
 }
 
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_reduce_balanced_kernel(const AttnPar
 
 constexpr int kBalancedWaves = 4;
 
-template <class E, int D, int B, bool PAGED, bool NT>
+template <class E, int D, int B, bool PAGED, int POL>
 int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.partition_size == PKV_PARTITION_BALANCED) {
         AttnParams q = p;
@@ -389,12 +403,12 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
         q.head_major = 0;
         int rc = balanced_check(q);
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves, NT>), dim3(q.balanced_wgs),
+        hipLaunchKernelGGL((attn_decode_balanced_kernel<E, D, B, PAGED, kBalancedWaves, POL>), dim3(q.balanced_wgs),
                            dim3(kBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, D, stream);
     }
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves, NT>), dim3(grid_parts, p.num_q_heads, num_seqs),
+    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves, POL>), dim3(grid_parts, p.num_q_heads, num_seqs),
                        dim3(kThreads), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "attention launch");
     if (rc || p.partition_size <= 0) return rc;
@@ -402,14 +416,15 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
 }
 
 template <class E, int D, bool PAGED>
-int dispatch_block(const AttnParams &p, int32_t block_size, bool cached, int32_t num_seqs, int32_t grid_parts,
+int dispatch_block(const AttnParams &p, int32_t block_size, int pol, int32_t num_seqs, int32_t grid_parts,
                    hipStream_t stream) {
     if constexpr (!PAGED) {
-        return launch<E, D, 16, false, true>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+        return launch<E, D, 16, false, kLoadStream>(p, num_seqs, grid_parts, stream);  // 16-row tiles
     } else {
-#define PKV_B(B) \
-    return cached ? launch<E, D, B, true, false>(p, num_seqs, grid_parts, stream) \
-                  : launch<E, D, B, true, true>(p, num_seqs, grid_parts, stream)
+#define PKV_B(B)                                                                                      \
+    return pol == kLoadCached  ? launch<E, D, B, true, kLoadCached>(p, num_seqs, grid_parts, stream) \
+           : pol == kLoadSplit ? launch<E, D, B, true, kLoadSplit>(p, num_seqs, grid_parts, stream)  \
+                               : launch<E, D, B, true, kLoadStream>(p, num_seqs, grid_parts, stream)
         switch (block_size) {
         case 8: PKV_B(8);
         case 16: PKV_B(16);
@@ -422,13 +437,13 @@ int dispatch_block(const AttnParams &p, int32_t block_size, bool cached, int32_t
 
 // One query head per workgroup (any G), then the merge pass of the split modes.
 template <bool PAGED>
-int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, bool cached,
+int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int pol,
                       int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     int rc;
 #define PKV_HD(E)                                                                                 \
     switch (head_dim) {                                                                           \
-    case 64: rc = dispatch_block<E, 64, PAGED>(p, block_size, cached, num_seqs, grid_parts, stream); break; \
-    case 128: rc = dispatch_block<E, 128, PAGED>(p, block_size, cached, num_seqs, grid_parts, stream); break; \
+    case 64: rc = dispatch_block<E, 64, PAGED>(p, block_size, pol, num_seqs, grid_parts, stream); break; \
+    case 128: rc = dispatch_block<E, 128, PAGED>(p, block_size, pol, num_seqs, grid_parts, stream); break; \
     default: return fail(PKV_EUNSUPPORTED, "head_dim %d not built (64, 128)", head_dim);          \
     }
     switch (dtype) {
@@ -444,10 +459,13 @@ int dispatch_per_head(const AttnParams &p, int32_t dtype, int32_t head_dim, int3
 template <bool PAGED>
 int dispatch(const AttnParams &p, int32_t dtype, int32_t head_dim, int32_t block_size, int32_t num_seqs,
              int32_t grid_parts, uint32_t flags, hipStream_t stream) {
-    const bool cached = PAGED && (flags & PKV_FLAG_CACHED_KV);
+    const int pol = !PAGED                          ? kLoadStream
+                    : (flags & PKV_FLAG_CACHED_KV) ? kLoadCached
+                    : p.cached_lens                ? kLoadSplit
+                                                   : kLoadStream;
     if (p.group > 1 && !(flags & PKV_FLAG_SCALAR_GQA) && gqa_mfma_supported(dtype, head_dim, block_size, p.group))
-        return launch_gqa_mfma(p, dtype, block_size, PAGED, cached, num_seqs, grid_parts, stream);
-    return dispatch_per_head<PAGED>(p, dtype, head_dim, block_size, cached, num_seqs, grid_parts, stream);
+        return launch_gqa_mfma(p, dtype, block_size, PAGED, pol, num_seqs, grid_parts, stream);
+    return dispatch_per_head<PAGED>(p, dtype, head_dim, block_size, pol, num_seqs, grid_parts, stream);
 }
 
 // Checks shared by the paged and contiguous entry points.
@@ -592,7 +610,8 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
                                           int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                                           int32_t partition_size, void *workspace, size_t workspace_bytes,
-                                          int32_t dtype, uint32_t flags, hipStream_t stream) {
+                                          int32_t dtype, uint32_t flags, const int32_t *cached_lens,
+                                          hipStream_t stream) {
     const char *fn = "pkv_paged_attention_decode";
     int rc = check_common(fn, out, q, k_cache, v_cache, context_lens, max_context_len, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, scale, partition_size, workspace, workspace_bytes, dtype);
@@ -609,6 +628,8 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (debug_validate()) {
         rc = validate_attention(fn, context_lens, num_seqs, max_context_len, block_tables, max_blocks_per_seq,
                                 block_size, num_blocks, 0, stream);
+        if (!rc && cached_lens && !(flags & PKV_FLAG_CACHED_KV))
+            rc = validate_device_array(fn, "cached_lens", cached_lens);
         if (rc) return rc;
     }
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
@@ -616,6 +637,7 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
                                partition_size, max_context_len, static_cast<int32_t>(cap), workspace,
                                workspace_bytes, head_dim);
     p.tables = block_tables;
+    p.cached_lens = cached_lens;
     p.max_blocks = max_blocks_per_seq;
     p.num_blocks = static_cast<uint32_t>(num_blocks);
     const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;

@@ -61,7 +61,7 @@ struct GqaLds {
 // The range's tiles go to the waves in stages of U tiles, round-robin. Each wave keeps NS
 // stages in registers: while it consumes one, the next NS - 1 are in flight, and the table
 // entries of the stage after those are on the way.
-template <class E, int B, bool PAGED, int W, int U, bool NT>
+template <class E, int B, bool PAGED, int W, int U, int POL>
 __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
                                  GqaLds<W> &lds) {
     using M = Mfma<E>;
@@ -94,6 +94,8 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
+    // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)
+    const int clen = POL == kLoadSplit ? __builtin_amdgcn_readfirstlane(p.cached_lens[s]) : 0;
 
     // the next stage this wave will issue (wave w takes stages w, w + W, w + 2W, ...: a fixed
     // assignment, so the summation order and the result do not depend on timing) and its
@@ -136,10 +138,17 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
             }
             const int rows = k < ntile && S.ok[u] ? min(TR, t1 - (jt0 + k) * TR) : 0;
             const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
+            if (POL == kLoadCached || (POL == kLoadSplit && (jt0 + k) * TR < clen)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<NT>(kr_, roff + i * ROWB);
+                for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<false>(kr_, roff + i * ROWB);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<NT>(vr_, roff + i * ROWB);
+                for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<false>(vr_, roff + i * ROWB);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<true>(kr_, roff + i * ROWB);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<true>(vr_, roff + i * ROWB);
+            }
         }
         cst += W;
         lookup();
@@ -286,7 +295,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 // so that a kv head's workgroups share XCDs (and the L2 holding a shared prefix). At most 256
 // registers per lane (two waves per SIMD): two workgroups share a CU and one's start-up hides
 // behind the other.
-template <class E, int B, bool PAGED, int W, int U, bool NT>
+template <class E, int B, bool PAGED, int W, int U, int POL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -307,14 +316,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         sink = Sink{p.ws + wr * 128, p.ws + p.ws_rows * 128 + wr, p.ws + p.ws_rows * 129 + wr,
                     static_cast<int64_t>(p.num_parts) * 128, p.num_parts};
     }
-    gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, t0, t1, sink, lds);
+    gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, t0, t1, sink, lds);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups (one per CU), each an equal share of the
 // batch's tiles (work rows = (kv head, sequence), head-major); cut rows are merged by the
 // balanced reduce pass. One workgroup per CU because two sharing a CU do not progress at one
 // pace (the older one's waves are served first), and the later one would finish alone.
-template <class E, int B, bool PAGED, int W, int U, bool NT>
+template <class E, int B, bool PAGED, int W, int U, int POL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -324,11 +333,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_zero_empty<E, 128, W * 64>(p, C);
     balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        gqa_range<E, B, PAGED, W, U, NT>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
+        gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
 }
 
-template <class E, int B, bool PAGED, bool NT>
+template <class E, int B, bool PAGED, int POL>
 int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.partition_size == PKV_PARTITION_BALANCED) {
         AttnParams q = p;
@@ -338,29 +347,33 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
         q.head_major = 1;  // an XCD's shares cover few kv heads: shared blocks stay in its L2
         int rc = balanced_check(q, 1);  // one workgroup per CU: two per CU would not run at one pace
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaBalancedWaves, kGqaTiles, NT>),
+        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaBalancedWaves, kGqaTiles, POL>),
                            dim3(q.balanced_wgs), dim3(kGqaBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "grouped-query attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
     }
-    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, NT>),
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, POL>),
                        dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
     if (rc || p.partition_size <= 0) return rc;
     return launch_reduce(p, E::CODE, 128, num_seqs, stream);
 }
 
+template <class E, int B>
+int launch_policy(const AttnParams &p, int pol, int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
+    if (pol == kLoadCached) return launch_one<E, B, true, kLoadCached>(p, num_seqs, grid_parts, stream);
+    if (pol == kLoadSplit) return launch_one<E, B, true, kLoadSplit>(p, num_seqs, grid_parts, stream);
+    return launch_one<E, B, true, kLoadStream>(p, num_seqs, grid_parts, stream);
+}
+
 template <class E, bool PAGED>
-int launch_block(const AttnParams &p, int32_t block_size, bool cached, int32_t num_seqs, int32_t grid_parts,
+int launch_block(const AttnParams &p, int32_t block_size, int pol, int32_t num_seqs, int32_t grid_parts,
                  hipStream_t stream) {
     if constexpr (!PAGED) {
-        return launch_one<E, 16, false, true>(p, num_seqs, grid_parts, stream);  // 16-row tiles
+        return launch_one<E, 16, false, kLoadStream>(p, num_seqs, grid_parts, stream);  // 16-row tiles
     } else {
-        if (block_size == 32)
-            return cached ? launch_one<E, 32, true, false>(p, num_seqs, grid_parts, stream)
-                          : launch_one<E, 32, true, true>(p, num_seqs, grid_parts, stream);
-        return cached ? launch_one<E, 16, true, false>(p, num_seqs, grid_parts, stream)
-                      : launch_one<E, 16, true, true>(p, num_seqs, grid_parts, stream);
+        return block_size == 32 ? launch_policy<E, 32>(p, pol, num_seqs, grid_parts, stream)
+                                : launch_policy<E, 16>(p, pol, num_seqs, grid_parts, stream);
     }
 }
 
@@ -371,16 +384,16 @@ bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int
            group >= 2 && group <= kMaxGroup;
 }
 
-int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, bool cached,
+int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int load_policy,
                     int32_t num_seqs, int32_t grid_parts, hipStream_t stream) {
     if (p.num_kv_heads > 65535 || grid_parts > 65535)
         return fail(PKV_EINVAL, "grouped-query attention: %d kv heads x %d partitions exceed the grid", p.num_kv_heads,
                     grid_parts);
     if (dtype == PKV_F16)
-        return paged ? launch_block<F16, true>(p, block_size, cached, num_seqs, grid_parts, stream)
-                     : launch_block<F16, false>(p, block_size, cached, num_seqs, grid_parts, stream);
-    return paged ? launch_block<BF16, true>(p, block_size, cached, num_seqs, grid_parts, stream)
-                 : launch_block<BF16, false>(p, block_size, cached, num_seqs, grid_parts, stream);
+        return paged ? launch_block<F16, true>(p, block_size, load_policy, num_seqs, grid_parts, stream)
+                     : launch_block<F16, false>(p, block_size, load_policy, num_seqs, grid_parts, stream);
+    return paged ? launch_block<BF16, true>(p, block_size, load_policy, num_seqs, grid_parts, stream)
+                 : launch_block<BF16, false>(p, block_size, load_policy, num_seqs, grid_parts, stream);
 }
 
 }  // namespace pkv

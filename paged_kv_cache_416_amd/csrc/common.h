@@ -31,6 +31,8 @@ bool debug_validate();
 // Lengths within [0, max_context_len] (and lmax when block_tables is NULL: the contiguous
 // layout), at most max_blocks blocks, every used table entry inside [0, num_blocks).
 // Synchronises `stream`; PKV_EINVAL with a message on the first violation.
+// PKV_DEBUG_VALIDATE: PKV_EINVAL unless dev points into device memory.
+int validate_device_array(const char *fn, const char *what, const void *dev);
 int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                        const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
                        int32_t lmax, hipStream_t stream);

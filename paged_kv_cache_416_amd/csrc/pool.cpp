@@ -306,6 +306,20 @@ int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_toke
     return PKV_OK;
 }
 
+int pkv_shared_prefix_lens(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t *out) {
+    if (!pool || n < 0 || (n > 0 && (!seq_ids || !out))) return fail(PKV_EINVAL, "pkv_shared_prefix_lens: bad arguments");
+    for (int32_t i = 0; i < n; ++i)
+        if (!pool->seqs.count(seq_ids[i]))
+            return fail(PKV_ENOSEQ, "pkv_shared_prefix_lens: unknown sequence %lld", (long long)seq_ids[i]);
+    for (int32_t i = 0; i < n; ++i) {
+        const auto &q = pool->seqs.find(seq_ids[i])->second;
+        int64_t j = 0;
+        while (j < static_cast<int64_t>(q.blocks.size()) && pool->ref[q.blocks[j]] > 1) ++j;
+        out[i] = static_cast<int32_t>(std::min<int64_t>({q.len, j * pool->block_size, INT32_MAX}));
+    }
+    return PKV_OK;
+}
+
 int pkv_build_block_tables(const pkv_pool *pool, const int64_t *seq_ids, int32_t n, int32_t max_blocks,
                            int32_t pad_value, int32_t *tables_out, int32_t *ctx_out) {
     if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !tables_out || !ctx_out)))

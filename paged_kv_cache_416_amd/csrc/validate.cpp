@@ -35,6 +35,15 @@ int fetch(const char *fn, const char *what, const T *dev, size_t n, hipStream_t 
 
 }  // namespace
 
+int validate_device_array(const char *fn, const char *what, const void *dev) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, dev) != hipSuccess || attr.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return fail(PKV_EINVAL, "%s: %s is not device memory (PKV_DEBUG_VALIDATE)", fn, what);
+    }
+    return PKV_OK;
+}
+
 int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                        const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
                        int32_t lmax, hipStream_t stream) {

@@ -109,9 +109,10 @@ def alloc_workspace(num_seqs, num_q_heads, head_dim, max_context_len, partition_
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                           partition_size=0, workspace=None, flags=0):
-    """out/q [S, Hq, D]; caches [N, Hkv, B, D]; block_tables int32 [S, max_blocks]; context_lens int32 [S]."""
-    _need_cuda(out, q, k_cache, v_cache, block_tables, context_lens, workspace)
+                           partition_size=0, workspace=None, flags=0, cached_lens=None):
+    """out/q [S, Hq, D]; caches [N, Hkv, B, D]; block_tables int32 [S, max_blocks]; context_lens int32 [S];
+    cached_lens: None or int32 [S], the load-policy hint (tokens per sequence in shared blocks)."""
+    _need_cuda(out, q, k_cache, v_cache, block_tables, context_lens, workspace, cached_lens)
     S, hq, d = q.shape
     N, hkv, B, d2 = k_cache.shape
     if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
@@ -125,11 +126,14 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("block_tables and context_lens must be int32")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if cached_lens is not None and (cached_lens.dtype != torch.int32 or cached_lens.shape != (S,)
+                                    or not cached_lens.is_contiguous()):
+        raise ValueError("cached_lens must be a contiguous int32 [S]")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     check(load().pkv_paged_attention_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N, _ptr(block_tables),
                                             block_tables.shape[1], _ptr(context_lens), int(max_context_len), S, hq,
                                             hkv, d, B, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
-                                            dtype_code(q.dtype), int(flags), _stream()))
+                                            dtype_code(q.dtype), int(flags), _ptr(cached_lens), _stream()))
     return out
 
 

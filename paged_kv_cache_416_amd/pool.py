@@ -106,6 +106,13 @@ class Pool:
                                                _i32p(ctx)))
         return tb, ctx
 
+    def shared_prefix_lens(self, sids):
+        """Tokens of each sequence in its leading shared blocks (count above one), int32 [n], host."""
+        ids = np.ascontiguousarray(sids, dtype=np.int64)
+        out = np.zeros(len(ids), np.int32)
+        check(self._lib.pkv_shared_prefix_lens(self._h, _i64p(ids), len(ids), _i32p(out)))
+        return out
+
     def migrate(self, dst: "Pool", sids):
         """Move sequences sids to pool dst, all or nothing -> (src block, dst block) pairs int32 [P, 2]
         to copy (preemption by swap and its recovery)."""

@@ -80,11 +80,11 @@ def gpu_replay(w, on_check=None):
     return c
 
 
-def gpu_attention(c, w, partition_size=None, flags=0, q=None):
+def gpu_attention(c, w, partition_size=None, flags=0, q=None, cached_lens=None):
     dt = TORCH_DTYPE[w.dtype]
     qd = to_device(w.q, dt, c.device) if q is None else q
     P = w.partition_size if partition_size is None else partition_size
-    out = c.attention(qd, w.batch, w.scale, partition_size=P, flags=flags)
+    out = c.attention(qd, w.batch, w.scale, partition_size=P, flags=flags, cached_lens=cached_lens)
     torch.cuda.synchronize()
     return out
 

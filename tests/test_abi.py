@@ -61,7 +61,7 @@ def _attn(**kw):
     return _lib.load().pkv_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["num_blocks"], a["tables"],
                                                   a["max_blocks"], a["ctx"], a["max_ctx"], a["S"], a["hq"], a["hkv"],
                                                   a["d"], a["B"], a["scale"], a["P"], a["ws"], a["ws_bytes"],
-                                                  a["dtype"], a["flags"], NULL)
+                                                  a["dtype"], a["flags"], NULL, NULL)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -100,8 +100,13 @@ def test_attention_matches_oracle(name):
         out = gpu_attention(c, w, partition_size=P)
         err = assert_close(out, ref, w.dtype, f"{name} P={P}")
         say(f"  [{name}] P={P} max abs err {err:.3e}")
-        # loading through the caches changes no arithmetic: bit-identical
+        # loading through the caches changes no arithmetic: bit-identical, whether every load or
+        # only the shared prefix (from the reference counts, or any values at all) goes through them
         assert bits_equal(gpu_attention(c, w, partition_size=P, flags=CACHED_KV), out)
+        assert bits_equal(gpu_attention(c, w, partition_size=P, cached_lens="shared"), out)
+        any_lens = torch.from_numpy(np.random.default_rng(P & 0xff).integers(-40, 3000, w.num_seqs,
+                                                                               dtype=np.int32)).cuda()
+        assert bits_equal(gpu_attention(c, w, partition_size=P, cached_lens=any_lens), out)
         if w.num_q_heads > w.num_kv_heads:
             out2 = gpu_attention(c, w, partition_size=P, flags=1)
             assert_close(out2, ref, w.dtype, f"{name} P={P} scalar-gqa")
@@ -184,6 +189,10 @@ def test_shared_prefix_equals_private_copies():
     assert all(c2.pool.ref_count(b) <= 1 for b in range(total + 4))
     private = gpu_attention(c2, w, partition_size=512)
     assert bits_equal(shared, private)
+    # the reference counts give each sequence its 64 shared prefix tokens, the private copies none
+    assert (c.pool.shared_prefix_lens(w.batch) == 64).all() and (c2.pool.shared_prefix_lens(w.batch) == 0).all()
+    for P in (0, 512, BALANCED):
+        assert bits_equal(gpu_attention(c, w, partition_size=P, cached_lens="shared"), gpu_attention(c, w, partition_size=P))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

@@ -77,6 +77,8 @@ class NativeVsModel(RuleBasedStateMachine):
             tb, ctx = self.native.tables(self.ids, pad=-7)
             mrows, mctx = self.model.tables(self.ids, tb.shape[1], pad=-7)
             assert tb.tolist() == mrows and ctx.tolist() == mctx
+            assert self.native.shared_prefix_lens(self.ids).tolist() == [self.model.shared_prefix_len(s)
+                                                                         for s in self.ids]
 
 
 NativeVsModel.TestCase.settings = settings(max_examples=150, stateful_step_count=50, deadline=None)
@@ -104,6 +106,9 @@ def test_error_codes():
     with pytest.raises(PkvError) as e:
         p.tables([1], max_blocks=0) if p.append([(1, 5)]) else None
     assert e.value.code == _lib.PKV_EINVAL
+    with pytest.raises(PkvError) as e:
+        p.shared_prefix_lens([1, 9])
+    assert e.value.code == _lib.PKV_ENOSEQ
 
 
 def test_all_or_nothing_on_exhaustion():

@@ -48,6 +48,42 @@ def test_cow_copies_n_minus_1_times():
             assert slots[b] == pool.blocks(b)[-1] * 16 + 37 % 16
 
 
+def test_shared_prefix_len_worked_example():
+    """Shared prefix from the counts, worked by hand: a 42-token sequence (blocks of 16: two full,
+    one holding 10) forked once shares all 42 tokens; the child's first append copies the shared
+    partial block (slide 13), after which both sequences share exactly the two full blocks."""
+    pool = BlockPool(16, 16)
+    pool.add(0)
+    pool.append([(0, 42)])
+    assert pool.shared_prefix_len(0) == 0  # nothing shared yet
+    pool.fork(0, 1)
+    assert pool.shared_prefix_len(0) == 42 and pool.shared_prefix_len(1) == 42
+    _, pairs = pool.append([(1, 1)])
+    assert len(pairs) == 1
+    assert pool.shared_prefix_len(0) == 32 and pool.shared_prefix_len(1) == 32
+    pool.append([(0, 30)])  # private tokens past the shared blocks
+    assert pool.shared_prefix_len(0) == 32 and pool.length(0) == 72
+    pool.fork(1, 2)  # sequence 1's third block (private until now) becomes shared too
+    assert pool.shared_prefix_len(1) == 43 and pool.shared_prefix_len(2) == 43
+    assert pool.shared_prefix_len(0) == 32
+    pool.free_seq(1)
+    pool.free_seq(2)
+    assert pool.shared_prefix_len(0) == 0
+    pool.check_invariants()
+
+
+def test_shared_prefix_len_stops_at_first_private_block():
+    """Blocks shared after a private one do not count: the hint is a prefix of the table."""
+    pool = BlockPool(8, 4)
+    pool.add("a")
+    pool.append([("a", 12)])
+    pool.fork("a", "b")
+    pool.append([("b", 4)])  # b: three shared full blocks + one private block
+    assert pool.shared_prefix_len("b") == 12 and pool.shared_prefix_len("a") == 12
+    pool.free_seq("a")
+    assert pool.shared_prefix_len("b") == 0
+
+
 def test_cow_not_needed_when_shared_block_is_full():
     pool = BlockPool(16, 16)
     pool.add(0)
