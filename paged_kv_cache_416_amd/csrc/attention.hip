@@ -41,7 +41,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 12;  // per-item schedule: one workgroup of three waves per SIMD on each CU
 constexpr int kThreads = kWaves * 64;
 
 template <class E, int D, int B>
@@ -49,10 +49,10 @@ struct Shape {
     static constexpr int VEC = E::VEC;                  // elements per 16-byte load
     static constexpr int LPR = D / VEC;                 // lanes per row
     static constexpr int RPI = 64 / LPR;                // rows per load instruction
-    static constexpr int TR = B < RPI * 8 ? B : RPI * 8;  // tile rows: at most 8 loads per lane per tile
+    static constexpr int TR = B < RPI * 4 ? B : RPI * 4;  // tile rows: at most 4 loads per lane per tile
     static constexpr int SPB = B / TR;                  // tiles per block
     static constexpr int NL = TR / RPI;                 // loads per lane per tile (K or V)
-    static constexpr int U = NL >= 8 ? 1 : 8 / NL;      // tiles per stage
+    static constexpr int U = 4 / NL;                    // tiles per stage: 4 K and 4 V loads per lane
     static constexpr int TILE_ELEMS = TR * D;
     static_assert(LPR >= 8 && LPR <= 64 && 64 % LPR == 0, "head_dim does not map onto a wave");
     static_assert(TR % RPI == 0 && B % TR == 0, "block_size must be a multiple of rows per load");
