@@ -57,9 +57,11 @@ typedef enum pkv_dtype {
 /* Attention flags. */
 #define PKV_FLAG_SCALAR_GQA 1u /* use the one-query-head-per-workgroup kernel even when G > 1 */
 /* The batch's sequences share blocks (a common prefix mapped by many block tables, slide 14:
- * a system prompt shared like a library): load K/V through the caches, so that a block's
+ * a system prompt shared like a library): load all K/V through the caches, so that a block's
  * re-reads by the other sequences hit the L2 / last-level cache. Without it K/V are streamed
- * past the caches (non-temporal), which suits blocks read once per call. Paged cache only. */
+ * past the caches (non-temporal), which suits blocks read once per call, except the tokens the
+ * cached_lens hint of pkv_paged_attention_decode names (the finer choice: only the shared
+ * prefix goes through the caches). Paged cache only. */
 #define PKV_FLAG_CACHED_KV 2u
 
 /* partition_size value for the balanced split: the library cuts the whole batch's work into
