@@ -21,6 +21,7 @@
 // falls free keeps its digest and contents until the pool needs it: free blocks without a
 // digest are handed out first (the LIFO stack), then hashed free blocks, least recently freed
 // first, each dropping its digest.
+#include <algorithm>
 #include <array>
 #include <cstring>
 #include <iterator>
