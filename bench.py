@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
+    ap.add_argument("--step", choices=["default", "fused", "separate"], default="default",
+                    help="a decode step as one launch (cache write + attention) or as the two calls; default: "
+                         "the faster one measured for the workload (one launch, except for the 8B GQA shape)")
     ap.add_argument("--cached-lens", choices=["default", "none", "shared"], default="default",
                     help="cached-load hint: none, or each sequence's shared prefix from the reference counts")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -215,6 +218,7 @@ def main():
     w, default_P, default_flags = make_workload(args.workload)
     flags = default_flags if args.flags < 0 else args.flags
     hint = args.cached_lens if args.cached_lens != "default" else ("shared" if args.workload == "gqa" else "none")
+    step_mode = args.step if args.step != "default" else ("separate" if args.workload == "gqa" else "fused")
     P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
     if P is None:
         P = int(args.partition)
@@ -251,21 +255,32 @@ def main():
         r = i % args.replicas
         kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, flags, cached_lens)
 
-    def one_step(i):
+    # a step's new rows in batch order (one token per sequence), for the one-launch step
+    assert [sid for sid, _, _ in step] == list(w.batch) and new_k.shape[0] == S
+    def separate_step(i):
         r = i % args.replicas
         kernels.reshape_and_cache(new_k, new_v, ks[r], vs[r], slot_dev)
         attend(i)
 
-    for i in range(args.warmup):
-        one_step(i)
-    torch.cuda.synchronize()
-    # timed region: exactly `steps` whole steps, synchronised on both sides, host clock
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    def fused_step(i):
+        r = i % args.replicas
+        kernels.paged_attention_decode_step(out, q, new_k, new_v, slot_dev, ks[r], vs[r], tb, ctx_dev, max_ctx,
+                                            w.scale, P, ws, flags, cached_lens)
+
+    def time_steps(fn, steps):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        # timed region: exactly `steps` whole steps, synchronised on both sides, host clock
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    one_step, other_step = (fused_step, separate_step) if step_mode == "fused" else (separate_step, fused_step)
+    ms_per_step = time_steps(one_step, args.steps)
+    ms_other = time_steps(other_step, args.steps)
     # the attention launches alone, for the roofline
     attn_us = timed_launches(attend, args.steps, stream)
     attn_pct = launch_percentiles(attend, max(100, args.steps), stream)
@@ -289,12 +304,14 @@ def main():
         "data": "synthetic (seeded N(0,1)*0.5 keys/values, seeded context lengths and physical block order)",
         "config": {"workload": w.name, "num_seqs": S, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": d,
                    "block_size": B, "sum_context": int(ctx.sum()), "max_context": int(ctx.max()),
-                   "partition_size": P, "flags": flags, "cached_lens": hint, "replicas": args.replicas},
+                   "partition_size": P, "flags": flags, "cached_lens": hint, "step": step_mode,
+                   "replicas": args.replicas},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "decode_tokens_per_s_attention_only": {
             "layers": LAYERS.get(w.name, 40),
             "value": round(S / (LAYERS.get(w.name, 40) * attn_us * 1e-6), 1)},
+        "ms_per_step_" + ("separate" if step_mode == "fused" else "fused"): round(ms_other, 5),
         "attention_us": round(attn_us, 2),
         "attention_us_single_launch": attn_pct,
         "bytes_per_step": {"attention_logical": logical_b, "attention_unique": unique_b, "cache_write": w_bytes},

@@ -287,6 +287,32 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
                                float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
                                int32_t dtype, uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
 
+/* One decode step in one launch: the cache write of pkv_reshape_and_cache for each sequence's new
+ * token, then pkv_paged_attention_decode over the cache with that token in it (slide 11: each step
+ * writes the new token's key and value into the free slot of the sequence's last block; slide 9:
+ * attention block by block). Results and cache bytes are those of the two calls in that order.
+ *  new_k, new_v:  device [num_seqs][num_kv_heads][head_dim] in dtype, contiguous, 16-byte aligned:
+ *                 the key and value of sequence s's token at position context_lens[s] - 1.
+ *  slot_mapping:  device int64[num_seqs]: that token's slot, block_tables[s][t / block_size] *
+ *                 block_size + t % block_size for t = context_lens[s] - 1 (pkv_seq_append gives
+ *                 it), or negative: not written, and attention reads that row from the cache
+ *                 (which must then hold the token already). A slot past num_blocks *
+ *                 block_size is treated as negative; a sequence of length 0 has no such token,
+ *                 so its slot must be negative.
+ *  k_cache, v_cache: written at those slots (one row per kv head) and read.
+ *  everything else: as for pkv_paged_attention_decode.
+ * Attention takes each sequence's last row from new_k/new_v rather than reading it back from the
+ * cache, so nothing in the launch reads what it writes. A slot that is not the slot of position
+ * context_lens[s] - 1 is a caller error (the results then differ from the two calls);
+ * PKV_DEBUG_VALIDATE=1 reports it as PKV_EINVAL, with the checks of the decode call. */
+int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k, const void *new_v,
+                                    const int64_t *slot_mapping, void *k_cache, void *v_cache, int64_t num_blocks,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                    int32_t dtype, uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
+
 /* Prefill (chunked) attention over the paged cache: the last n_s = query_start[s+1] -
  * query_start[s] tokens of each sequence s are queries, and query i of s, at position
  * p = context_lens[s] - n_s + i, attends causally to the keys at positions 0 .. p, earlier

@@ -90,6 +90,12 @@ struct AttnParams {
     const int32_t *tables;
     const int32_t *ctx_lens;
     const int32_t *cached_lens;  // kLoadSplit: per sequence, tokens [0, n) are loaded through the caches
+    // decode step with the cache write: sequence s's new key and value rows (its token at position
+    // length - 1, [S][Hkv][D]) and their slot; null new_k for attention alone
+    const void *new_k;
+    const void *new_v;
+    const int64_t *new_slots;
+    int64_t num_slots;  // num_blocks * block_size: a slot at or past it is not written
     float *ws;             // split workspace: acc [S*Hq*P][D], then m [S*Hq*P], then l [S*Hq*P]
     int64_t ws_rows;       // S * Hq * num_parts
     uint32_t num_blocks;   // paged: pool size (< 2^31)
@@ -192,6 +198,29 @@ __device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_
         uint32_t *out = balanced_prefix_out(p);
         for (int i = t; i <= S; i += NT) out[i] = C[i];
     }
+}
+
+// Decode step with the cache write: 16-byte chunk `chunk` of sequence s's new key and value rows
+// for kv head kvh goes to the token's slot (slide 11: a new token goes into the free slot of its
+// sequence's last block). Called only where new_row_position(p, s) >= 0 (a slot inside the pool).
+// Nothing in the launch reads what this writes: attention takes that row from new_k/new_v.
+template <int B, int ROWB>
+__device__ inline void store_new_row(const AttnParams &p, int s, int kvh, int chunk, const u32x4 &k, const u32x4 &v) {
+    const int64_t slot = p.new_slots[s];
+    const int64_t blk = slot / B, off = slot - blk * B;
+    const int64_t dst = ((blk * p.num_kv_heads + kvh) * B + off) * ROWB + chunk * 16;
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(const_cast<void *>(p.k)) + dst) = k;
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(const_cast<void *>(p.v)) + dst) = v;
+}
+
+// Decode step with the cache write: the position of sequence s's new token if this launch writes
+// it (a slot inside the pool, a non-empty sequence), else -1 (attention alone, or a row the cache
+// already holds: a negative slot, which an empty sequence must have). Uniform.
+__device__ inline int new_row_position(const AttnParams &p, int s) {
+    if (!p.new_k) return -1;
+    const int64_t slot = p.new_slots[s];
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    return __builtin_amdgcn_readfirstlane(slot >= 0 && slot < p.num_slots && ctx > 0 ? ctx - 1 : -1);
 }
 
 // Outputs of sequences with no tokens are zeros; the workgroups share them out.

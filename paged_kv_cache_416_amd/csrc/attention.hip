@@ -67,10 +67,11 @@ struct MhaLds {
 
 // Tokens [t0, t1) of sequence s for query head h (t0 a multiple of the tile rows, t0 < t1 <= the
 // length): the workgroup's merged result goes to sink. Uniform over the workgroup; ends with a
-// barrier, so the caller may run it again on the same LDS.
+// barrier, so the caller may run it again on the same LDS. In a decode step with the cache write,
+// the one caller per (sequence, kv head) that passes write_new stores the sequence's new rows.
 template <class E, int D, int B, bool PAGED, int W, int POL>
 __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int t1, const Sink &sink,
-                                 MhaLds<W, D> &lds) {
+                                 MhaLds<W, D> &lds, bool write_new) {
     using SH = Shape<E, D, B>;
     constexpr int VEC = SH::VEC, LPR = SH::LPR, RPI = SH::RPI, TR = SH::TR, SPB = SH::SPB, NL = SH::NL,
                   U = SH::U;
@@ -97,6 +98,16 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
     // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)
     const int clen = POL == kLoadSplit ? __builtin_amdgcn_readfirstlane(p.cached_lens[s]) : 0;
     const u32x4 qv = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + (row_q * D + c * VEC) * E::ELT);
+    // decode step with the cache write: the sequence's last row (its new token), when this launch
+    // writes it, comes from the new key and value rows (chunk c in every lane), not from the cache
+    // (the loads go out without waiting for the position, which is first needed at the last stage)
+    const int last = new_row_position(p, s);
+    u32x4 knew = {0u, 0u, 0u, 0u}, vnew = {0u, 0u, 0u, 0u};
+    if (p.new_k) {
+        const int64_t nrow = (static_cast<int64_t>(s) * p.num_kv_heads + kvh) * D + c * VEC;
+        knew = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.new_k) + nrow * E::ELT);
+        vnew = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.new_v) + nrow * E::ELT);
+    }
 
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
@@ -166,7 +177,21 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
 
-    auto consume = [&](const Stage &S, bool tail) {
+    auto consume = [&](Stage &S, bool tail) {
+        if (tail && last >= 0) {  // the last row lies in a wave's last stage
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (S.tok0[u] > last || last >= S.tok0[u] + TR) continue;  // uniform
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    // the row this lane loaded: rows at or past t1 were clamped to row t1 - 1, and
+                    // their zero weights would not cancel a stale value there (0 * NaN = NaN)
+                    const bool mine = S.tok0[u] + min(l * RPI + r0, t1 - 1 - S.tok0[u]) == last;
+                    S.k[u][l] = mine ? knew : S.k[u][l];
+                    S.v[u][l] = mine ? vnew : S.v[u][l];
+                }
+            }
+        }
         float sc[U][NL];
         float mloc = -INFINITY;
 #pragma unroll
@@ -286,6 +311,9 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
         }
     }
     __syncthreads();
+    // after the barrier, which would otherwise wait for these stores to complete
+    if (write_new && last >= 0 && wave == 0 && lane < LPR)  // lanes 0 .. LPR-1 hold the whole row
+        store_new_row<B, D * E::ELT>(p, s, kvh, c, knew, vnew);
 }
 
 // Per-item schedule: grid = (parts, num_q_heads, num_seqs), block = 64 * W; one workgroup per
@@ -308,7 +336,8 @@ __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p)
         const int64_t wr = row_q * p.num_parts + part;
         sink = Sink{p.ws + wr * D, p.ws + p.ws_rows * D + wr, p.ws + p.ws_rows * (D + 1) + wr, 0, 0};
     }
-    mha_range<E, D, B, PAGED, W, POL>(p, s, h, t0, t1, sink, lds);
+    // one workgroup per (sequence, kv head) writes the new rows of a decode step
+    mha_range<E, D, B, PAGED, W, POL>(p, s, h, t0, t1, sink, lds, t0 == 0 && h % p.group == 0);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups, each an equal share of the batch's tiles
@@ -324,7 +353,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_walk<D, false>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        mha_range<E, D, B, PAGED, W, POL>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds);
+        // the share holding a row's first tile writes the new rows of a decode step
+        mha_range<E, D, B, PAGED, W, POL>(p, s, h, ta * TR, min(tb * TR, ctx), sink, lds, ta == 0 && h % p.group == 0);
     });
 }
 
@@ -604,15 +634,17 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
     return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
-extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                                          int64_t num_blocks, const int32_t *block_tables,
-                                          int32_t max_blocks_per_seq, const int32_t *context_lens,
-                                          int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                                          int32_t partition_size, void *workspace, size_t workspace_bytes,
-                                          int32_t dtype, uint32_t flags, const int32_t *cached_lens,
-                                          hipStream_t stream) {
-    const char *fn = "pkv_paged_attention_decode";
+namespace pkv {
+namespace {
+
+// The paged decode entry points: attention alone (new_k == nullptr), or a decode step that also
+// writes each sequence's new key and value rows to their slots in the same launch.
+int paged_decode(const char *fn, void *out, const void *q, const void *k_cache, const void *v_cache,
+                 int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale, int32_t partition_size,
+                 void *workspace, size_t workspace_bytes, int32_t dtype, uint32_t flags, const int32_t *cached_lens,
+                 const void *new_k, const void *new_v, const int64_t *slot_mapping, hipStream_t stream) {
     int rc = check_common(fn, out, q, k_cache, v_cache, context_lens, max_context_len, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, scale, partition_size, workspace, workspace_bytes, dtype);
     if (rc || num_seqs == 0) return rc;
@@ -625,11 +657,16 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     if (!block_tables || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return fail(PKV_EINVAL, "%s: block_tables NULL or max_blocks_per_seq / num_blocks not positive", fn);
     if (num_blocks > INT32_MAX) return fail(PKV_EINVAL, "%s: num_blocks %lld exceeds int32", fn, (long long)num_blocks);
+    if (new_k && (!new_v || !slot_mapping || !aligned16(new_k) || !aligned16(new_v)))
+        return fail(PKV_EINVAL, "%s: new_k, new_v (16-byte aligned) and slot_mapping are needed", fn);
     if (debug_validate()) {
         rc = validate_attention(fn, context_lens, num_seqs, max_context_len, block_tables, max_blocks_per_seq,
                                 block_size, num_blocks, 0, stream);
         if (!rc && cached_lens && !(flags & PKV_FLAG_CACHED_KV))
             rc = validate_device_array(fn, "cached_lens", cached_lens);
+        if (!rc && new_k)
+            rc = validate_step_slots(fn, slot_mapping, context_lens, block_tables, num_seqs, max_blocks_per_seq,
+                                     block_size, stream);
         if (rc) return rc;
     }
     const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size);
@@ -640,8 +677,46 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     p.cached_lens = cached_lens;
     p.max_blocks = max_blocks_per_seq;
     p.num_blocks = static_cast<uint32_t>(num_blocks);
+    p.new_k = new_k;
+    p.new_v = new_v;
+    p.new_slots = slot_mapping;
+    p.num_slots = num_blocks * block_size;
     const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
     return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, flags, stream);
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                          int64_t num_blocks, const int32_t *block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                          int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                                          int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                          int32_t dtype, uint32_t flags, const int32_t *cached_lens,
+                                          hipStream_t stream) {
+    return paged_decode("pkv_paged_attention_decode", out, q, k_cache, v_cache, num_blocks, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                        head_dim, block_size, scale, partition_size, workspace, workspace_bytes, dtype, flags,
+                        cached_lens, nullptr, nullptr, nullptr, stream);
+}
+
+extern "C" int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k, const void *new_v,
+                                               const int64_t *slot_mapping, void *k_cache, void *v_cache,
+                                               int64_t num_blocks, const int32_t *block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                               int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               float scale, int32_t partition_size, void *workspace,
+                                               size_t workspace_bytes, int32_t dtype, uint32_t flags,
+                                               const int32_t *cached_lens, hipStream_t stream) {
+    const char *fn = "pkv_paged_attention_decode_step";
+    if (num_seqs > 0 && (!new_k || !new_v || !slot_mapping)) return fail(PKV_EINVAL, "%s: NULL pointer", fn);
+    return paged_decode(fn, out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                        max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                        partition_size, workspace, workspace_bytes, dtype, flags, cached_lens, new_k, new_v,
+                        slot_mapping, stream);
 }
 
 extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, const void *v, int32_t lmax,

@@ -33,6 +33,11 @@ bool debug_validate();
 // Synchronises `stream`; PKV_EINVAL with a message on the first violation.
 // PKV_DEBUG_VALIDATE: PKV_EINVAL unless dev points into device memory.
 int validate_device_array(const char *fn, const char *what, const void *dev);
+// PKV_DEBUG_VALIDATE for a decode step with the cache write: each non-negative slot_mapping[s] is
+// the slot of position context_lens[s] - 1 through the block table.
+int validate_step_slots(const char *fn, const int64_t *slot_mapping, const int32_t *context_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t max_blocks, int32_t block_size,
+                        hipStream_t stream);
 int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                        const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
                        int32_t lmax, hipStream_t stream);

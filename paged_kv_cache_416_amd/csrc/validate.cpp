@@ -44,6 +44,29 @@ int validate_device_array(const char *fn, const char *what, const void *dev) {
     return PKV_OK;
 }
 
+int validate_step_slots(const char *fn, const int64_t *slot_mapping, const int32_t *context_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t max_blocks, int32_t block_size,
+                        hipStream_t stream) {
+    std::vector<int64_t> slots;
+    std::vector<int32_t> ctx, tab;
+    int rc = fetch(fn, "slot_mapping", slot_mapping, static_cast<size_t>(num_seqs), stream, slots);
+    if (!rc) rc = fetch(fn, "context_lens", context_lens, static_cast<size_t>(num_seqs), stream, ctx);
+    if (!rc) rc = fetch(fn, "block_tables", block_tables, static_cast<size_t>(num_seqs) * max_blocks, stream, tab);
+    if (rc) return rc;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        if (slots[s] < 0) continue;
+        const int32_t t = ctx[s] - 1;  // the new token's position (lengths already checked)
+        const int64_t want = t < 0 ? -1
+                                   : static_cast<int64_t>(tab[static_cast<size_t>(s) * max_blocks + t / block_size]) *
+                                             block_size + t % block_size;
+        if (slots[s] != want)
+            return fail(PKV_EINVAL,
+                        "%s: slot_mapping[%d] = %lld is not the slot of position context_lens[%d] - 1 (%lld) "
+                        "(PKV_DEBUG_VALIDATE)", fn, s, static_cast<long long>(slots[s]), s, static_cast<long long>(want));
+    }
+    return PKV_OK;
+}
+
 int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                        const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
                        int32_t lmax, hipStream_t stream) {

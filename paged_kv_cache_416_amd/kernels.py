@@ -137,6 +137,40 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def paged_attention_decode_step(out, q, new_k, new_v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                                max_context_len, scale, partition_size=0, workspace=None, flags=0, cached_lens=None):
+    """reshape_and_cache(new_k, new_v, slot_mapping) then paged_attention_decode, in one launch.
+    new_k/new_v [S, Hkv, D] (sequence s's token at position context_lens[s] - 1); slot_mapping int64 [S]."""
+    _need_cuda(out, q, new_k, new_v, slot_mapping, k_cache, v_cache, block_tables, context_lens, workspace,
+               cached_lens)
+    S, hq, d = q.shape
+    N, hkv, B, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    if new_k.shape != (S, hkv, d) or new_v.shape != new_k.shape or slot_mapping.shape != (S,):
+        raise ValueError("new_k/new_v must be [S, Hkv, D] and slot_mapping [S]")
+    for t in (out, q, new_k, new_v, slot_mapping, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if len({t.dtype for t in (out, q, new_k, new_v, k_cache, v_cache)}) != 1:
+        raise ValueError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or slot_mapping.dtype != torch.int64:
+        raise ValueError("block_tables and context_lens must be int32, slot_mapping int64")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if cached_lens is not None and (cached_lens.dtype != torch.int32 or cached_lens.shape != (S,)
+                                    or not cached_lens.is_contiguous()):
+        raise ValueError("cached_lens must be a contiguous int32 [S]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(load().pkv_paged_attention_decode_step(_ptr(out), _ptr(q), _ptr(new_k), _ptr(new_v), _ptr(slot_mapping),
+                                                 _ptr(k_cache), _ptr(v_cache), N, _ptr(block_tables),
+                                                 block_tables.shape[1], _ptr(context_lens), int(max_context_len), S,
+                                                 hq, hkv, d, B, float(scale), int(partition_size), _ptr(workspace),
+                                                 ws_bytes, dtype_code(q.dtype), int(flags), _ptr(cached_lens),
+                                                 _stream()))
+    return out
+
+
 def contiguous_attention_decode(out, q, k, v, context_lens, max_context_len, scale, partition_size=0,
                                 workspace=None, flags=0):
     """out/q [S, Hq, D]; k, v [S, Hkv, Lmax, D]; context_lens int32 [S]."""
