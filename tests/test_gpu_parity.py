@@ -351,11 +351,12 @@ def test_balanced_at_the_sequence_limit(dtype, hq, hkv, d):
     assert e.value.code == PKV_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("one_launch", [False, True])
 @pytest.mark.parametrize("P", [0, BALANCED])
-def test_decode_step_in_a_hip_graph(P):
-    """One decode step (cache write + attention) captured in a graph and replayed with new inputs
-    between replays (eager work in between): every replay equals the same step run eagerly, bit
-    for bit."""
+def test_decode_step_in_a_hip_graph(P, one_launch):
+    """One decode step (cache write + attention, as two calls or in one launch) captured in a graph
+    and replayed with new inputs between replays (eager work in between): every replay equals the
+    same step run eagerly, bit for bit, and the one-launch step equals the two calls."""
     w = synth.llama13b(num_seqs=6, ctx_range=(40, 900))
     dt = TORCH_DTYPE[w.dtype]
     c = gpu_replay(w)
@@ -370,9 +371,14 @@ def test_decode_step_in_a_hip_graph(P):
     out = torch.empty_like(q)
     ws = kernels.alloc_workspace(S, w.num_q_heads, d, mx, P, c.device)
 
-    def step(o):
+    def two_calls(o):
         kernels.reshape_and_cache(new_k, new_v, c.k, c.v, slots)
         kernels.paged_attention_decode(o, q, c.k, c.v, tb, ctx, mx, w.scale, P, ws, 0)
+
+    def one_call(o):
+        kernels.paged_attention_decode_step(o, q, new_k, new_v, slots, c.k, c.v, tb, ctx, mx, w.scale, P, ws, 0)
+
+    step = one_call if one_launch else two_calls
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -393,8 +399,11 @@ def test_decode_step_in_a_hip_graph(P):
         from_graph = out.clone()
         eager = torch.empty_like(out)
         step(eager)
+        other = torch.empty_like(out)
+        (two_calls if one_launch else one_call)(other)
         torch.cuda.synchronize()
         assert bits_equal(from_graph, eager), f"replay {i}"
+        assert bits_equal(from_graph, other), f"replay {i}: one launch and two calls differ"
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 4, 4, 128), ("bf16", 8, 2, 128), ("f32", 4, 2, 64),
