@@ -96,6 +96,8 @@ struct AttnParams {
     const void *new_v;
     const int64_t *new_slots;
     int64_t num_slots;  // num_blocks * block_size: a slot at or past it is not written
+    void *k_write;      // the caches again, writable (k and v above), for the new rows
+    void *v_write;
     float *ws;             // split workspace: acc [S*Hq*P][D], then m [S*Hq*P], then l [S*Hq*P]
     int64_t ws_rows;       // S * Hq * num_parts
     uint32_t num_blocks;   // paged: pool size (< 2^31)
@@ -209,8 +211,8 @@ __device__ inline void store_new_row(const AttnParams &p, int s, int kvh, int ch
     const int64_t slot = p.new_slots[s];
     const int64_t blk = slot / B, off = slot - blk * B;
     const int64_t dst = ((blk * p.num_kv_heads + kvh) * B + off) * ROWB + chunk * 16;
-    *reinterpret_cast<u32x4 *>(static_cast<char *>(const_cast<void *>(p.k)) + dst) = k;
-    *reinterpret_cast<u32x4 *>(static_cast<char *>(const_cast<void *>(p.v)) + dst) = v;
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(p.k_write) + dst) = k;
+    *reinterpret_cast<u32x4 *>(static_cast<char *>(p.v_write) + dst) = v;
 }
 
 // Decode step with the cache write: the position of sequence s's new token if this launch writes

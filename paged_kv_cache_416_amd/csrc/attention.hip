@@ -644,7 +644,8 @@ int paged_decode(const char *fn, void *out, const void *q, const void *k_cache, 
                  const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale, int32_t partition_size,
                  void *workspace, size_t workspace_bytes, int32_t dtype, uint32_t flags, const int32_t *cached_lens,
-                 const void *new_k, const void *new_v, const int64_t *slot_mapping, hipStream_t stream) {
+                 const void *new_k, const void *new_v, const int64_t *slot_mapping, void *k_write, void *v_write,
+                 hipStream_t stream) {
     int rc = check_common(fn, out, q, k_cache, v_cache, context_lens, max_context_len, num_seqs, num_q_heads,
                           num_kv_heads, head_dim, scale, partition_size, workspace, workspace_bytes, dtype);
     if (rc || num_seqs == 0) return rc;
@@ -681,6 +682,8 @@ int paged_decode(const char *fn, void *out, const void *q, const void *k_cache, 
     p.new_v = new_v;
     p.new_slots = slot_mapping;
     p.num_slots = num_blocks * block_size;
+    p.k_write = k_write;
+    p.v_write = v_write;
     const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
     return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, flags, stream);
 }
@@ -699,7 +702,7 @@ extern "C" int pkv_paged_attention_decode(void *out, const void *q, const void *
     return paged_decode("pkv_paged_attention_decode", out, q, k_cache, v_cache, num_blocks, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
                         head_dim, block_size, scale, partition_size, workspace, workspace_bytes, dtype, flags,
-                        cached_lens, nullptr, nullptr, nullptr, stream);
+                        cached_lens, nullptr, nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 extern "C" int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k, const void *new_v,
@@ -716,7 +719,7 @@ extern "C" int pkv_paged_attention_decode_step(void *out, const void *q, const v
     return paged_decode(fn, out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, context_lens,
                         max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale,
                         partition_size, workspace, workspace_bytes, dtype, flags, cached_lens, new_k, new_v,
-                        slot_mapping, stream);
+                        slot_mapping, k_cache, v_cache, stream);
 }
 
 extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const void *k, const void *v, int32_t lmax,
