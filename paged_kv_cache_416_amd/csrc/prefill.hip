@@ -27,6 +27,7 @@ constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowTiles = 2;  // 16-row tiles per wave
 constexpr int kStepKeys = 32;        // keys per step (two 16-key tiles)
 constexpr int kLdsRow = 272;         // bytes per staged row: 256 + 16 of padding
+constexpr float kMaxSlack = 8.f;     // log2 units the softmax reference may lag the running maximum
 
 struct PrefillParams {
     void *out;
@@ -75,6 +76,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         head[rt] = kvh * G + (row_ok[rt] ? r % G : 0);
         qpos[rt] = ctx - nq + tok[rt];
     }
+    // the position of each row tile's first row: no row of the tile sees fewer keys
+    int qmin[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) qmin[rt] = ctx - nq + (row0 + rt * 16) / G;
     // keys the workgroup needs: [0, kend); keys this wave's rows need: [0, kend_w)
     const int kend = __builtin_amdgcn_readfirstlane(ctx - nq + min(wg_row0 + W * RT * 16 - 1, rows - 1) / G + 1);
     const int kend_w = row0 < rows ? ctx - nq + min(row0 + RT * 16 - 1, rows - 1) / G + 1 : 0;
@@ -170,22 +175,43 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float sc[2][4], mloc = -INFINITY;
+            // a step wholly before the tile's first row (and inside the pool) needs no mask
+            // (uniform: the rows' positions grow with the row index)
+            const bool open = (t + 1) * kStepKeys - 1 <= qmin[rt] && ok[0] && ok[1];
+            if (open) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kpos = t * kStepKeys + u * TR + 4 * g + i;  // qpos < kend: kend is implied
-                    sc[u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
-                    mloc = fmaxf(mloc, sc[u][i]);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        sc[u][i] = c[rt][u][i] * p.scale_log2;
+                        mloc = fmaxf(mloc, sc[u][i]);
+                    }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kpos = t * kStepKeys + u * TR + 4 * g + i;  // qpos < kend: kend is implied
+                        sc[u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
+                        mloc = fmaxf(mloc, sc[u][i]);
+                    }
+            }
             mloc = max_over_lane_groups(mloc);
+            // m[rt] is the reference the weights are taken against, exp2(s - m). It moves to the
+            // running maximum only when some row's maximum passes it by more than kMaxSlack, so the
+            // rescale is rare; the weights stay below 2^kMaxSlack, and the quotient acc / l does not
+            // depend on the reference.
             const float m_new = fmaxf(m[rt], mloc);
-            const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-            if (__builtin_amdgcn_ballot_w64(m_new > m[rt]) != 0) {
+            float m_ref;
+            if (__builtin_amdgcn_ballot_w64(m_new > m[rt] + kMaxSlack) != 0) {
+                m_ref = m_new == -INFINITY ? 0.f : m_new;
                 const float alpha = fast_exp2(m[rt] - m_ref);
                 lsum[rt] *= alpha;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[rt][j] *= alpha;
+                m[rt] = m_new;
+            } else {
+                m_ref = m[rt] == -INFINITY ? 0.f : m[rt];
             }
             unsigned h[4], r[4];  // weights of keys (u, 2w), (u, 2w + 1) in word 2u + w
 #pragma unroll
@@ -214,7 +240,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                                   __builtin_amdgcn_perm(word(vf[1][3], w), word(vf[1][2], w), sel)};
                 acc[rt][j] = M::mma(vt, pr, M::mma(vt, ph, acc[rt][j]));
             }
-            m[rt] = m_new;
         }
     };
 
