@@ -99,9 +99,8 @@ def parse():
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flags", type=int, default=-1, help="attention flags; -1 = the workload's default")
-    ap.add_argument("--step", choices=["default", "fused", "separate"], default="default",
-                    help="a decode step as one launch (cache write + attention) or as the two calls; default: "
-                         "the faster one measured for the workload (one launch, except for the 8B GQA shape)")
+    ap.add_argument("--step", choices=["fused", "separate"], default="fused",
+                    help="a decode step as one call (pkv_paged_attention_decode_step) or as the two calls")
     ap.add_argument("--cached-lens", choices=["default", "none", "shared"], default="default",
                     help="cached-load hint: none, or each sequence's shared prefix from the reference counts")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -218,7 +217,7 @@ def main():
     w, default_P, default_flags = make_workload(args.workload)
     flags = default_flags if args.flags < 0 else args.flags
     hint = args.cached_lens if args.cached_lens != "default" else ("shared" if args.workload == "gqa" else "none")
-    step_mode = args.step if args.step != "default" else ("separate" if args.workload == "gqa" else "fused")
+    step_mode = args.step
     P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
     if P is None:
         P = int(args.partition)
@@ -279,6 +278,11 @@ def main():
         return (time.perf_counter() - t0) * 1e3 / steps
 
     one_step, other_step = (fused_step, separate_step) if step_mode == "fused" else (separate_step, fused_step)
+    # both forms run before either is timed: the first timed loop of a process otherwise runs
+    # about 1 % slow (measured with either form first), which would favour the second
+    for i in range(args.warmup):
+        other_step(i)
+        one_step(i)
     ms_per_step = time_steps(one_step, args.steps)
     ms_other = time_steps(other_step, args.steps)
     # the attention launches alone, for the roofline

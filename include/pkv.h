@@ -287,10 +287,12 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
                                float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
                                int32_t dtype, uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
 
-/* One decode step in one launch: the cache write of pkv_reshape_and_cache for each sequence's new
+/* One decode step in one call: the cache write of pkv_reshape_and_cache for each sequence's new
  * token, then pkv_paged_attention_decode over the cache with that token in it (slide 11: each step
  * writes the new token's key and value into the free slot of the sequence's last block; slide 9:
  * attention block by block). Results and cache bytes are those of the two calls in that order.
+ * One launch on the one-query-head kernel; the grouped-query matrix-core path writes the new rows
+ * with a launch of its own first (measured faster there).
  *  new_k, new_v:  device [num_seqs][num_kv_heads][head_dim] in dtype, contiguous, 16-byte aligned:
  *                 the key and value of sequence s's token at position context_lens[s] - 1.
  *  slot_mapping:  device int64[num_seqs]: that token's slot, block_tables[s][t / block_size] *
@@ -301,8 +303,8 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
  *                 so its slot must be negative.
  *  k_cache, v_cache: written at those slots (one row per kv head) and read.
  *  everything else: as for pkv_paged_attention_decode.
- * Attention takes each sequence's last row from new_k/new_v rather than reading it back from the
- * cache, so nothing in the launch reads what it writes. A slot that is not the slot of position
+ * In one launch, attention takes each sequence's last row from new_k/new_v rather than reading it
+ * back from the cache, so nothing in the launch reads what it writes. A slot that is not the slot of position
  * context_lens[s] - 1 is a caller error (the results then differ from the two calls);
  * PKV_DEBUG_VALIDATE=1 reports it as PKV_EINVAL, with the checks of the decode call. */
 int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k, const void *new_v,

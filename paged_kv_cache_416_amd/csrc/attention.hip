@@ -685,6 +685,18 @@ int paged_decode(const char *fn, void *out, const void *q, const void *k_cache, 
     p.k_write = k_write;
     p.v_write = v_write;
     const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
+    if (new_k && p.group > 1 && !(flags & PKV_FLAG_SCALAR_GQA) &&
+        gqa_mfma_supported(dtype, head_dim, block_size, p.group)) {
+        // the grouped-query matrix-core path writes the new rows with its own launch first (one
+        // launch measured slower there: the substitution sits in its matrix-core loop), then
+        // attends over the cache that holds them
+        rc = pkv_reshape_and_cache(new_k, new_v, static_cast<int64_t>(num_kv_heads) * head_dim,
+                                   static_cast<int64_t>(num_kv_heads) * head_dim, k_write, v_write, num_blocks,
+                                   slot_mapping, num_seqs, num_kv_heads, head_dim, block_size, dtype, stream);
+        if (rc) return rc;
+        p.new_k = p.new_v = nullptr;
+        p.new_slots = nullptr;
+    }
     return dispatch<true>(p, dtype, head_dim, block_size, num_seqs, grid_parts, flags, stream);
 }
 

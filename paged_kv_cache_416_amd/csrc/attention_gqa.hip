@@ -56,15 +56,14 @@ struct GqaLds {
 // Tokens [t0, t1) of sequence s for kv head kvh and its G query heads (t0 a multiple of 16,
 // t0 < t1 <= the length): the workgroup's merged result goes to sink. Uniform over the
 // workgroup; ends with a barrier, so the caller may run it again on the same LDS. head_dim 128,
-// 16-bit types. In a decode step with the cache write, the one caller per (sequence, kv head)
-// that passes write_new stores the sequence's new rows.
+// 16-bit types.
 //
 // The range's tiles go to the waves in stages of U tiles, round-robin. Each wave keeps NS
 // stages in registers: while it consumes one, the next NS - 1 are in flight, and the table
 // entries of the stage after those are on the way.
 template <class E, int B, bool PAGED, int W, int U, int POL>
 __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
-                                 GqaLds<W> &lds, bool write_new) {
+                                 GqaLds<W> &lds) {
     using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;          // tile rows
@@ -95,12 +94,6 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 
     const char *kc = static_cast<const char *>(p.k);
     const char *vc = static_cast<const char *>(p.v);
-    // decode step with the cache write: the sequence's last row (its new token), when this launch
-    // writes it, comes from the new key and value rows (chunk n in every lane), not from the cache;
-    // they are loaded where the tile holding that row is consumed, once per range
-    const int last = new_row_position(p, s);
-    const char *nk = p.new_k ? static_cast<const char *>(p.new_k) + ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * D + n * 8) * 2 : nullptr;
-    const char *nv = p.new_k ? static_cast<const char *>(p.new_v) + ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * D + n * 8) * 2 : nullptr;
     // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)
     const int clen = POL == kLoadSplit ? __builtin_amdgcn_readfirstlane(p.cached_lens[s]) : 0;
 
@@ -184,22 +177,12 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         float mloc = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t0u = (jt0 + S.st * U + u) * TR;  // a stand-in's rows all lie past t1
-            if (last >= t0u && last < t0u + TR) {      // uniform
-                const u32x4 knew = *reinterpret_cast<const u32x4 *>(nk), vnew = *reinterpret_cast<const u32x4 *>(nv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool mine = t0u + 4 * g + i == last;
-                    S.k[u][i] = mine ? knew : S.k[u][i];
-                    S.v[u][i] = mine ? vnew : S.v[u][i];
-                }
-            }
             u32x4 ka[4];
             k_operand(S.k[u], ka);
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
-            const int tok0 = t0u;
+            const int tok0 = (jt0 + S.st * U + u) * TR;  // a stand-in's rows all lie past t1
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool valid = S.ok[u] && tok0 + 4 * g + i < t1;
@@ -306,9 +289,6 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
         }
     }
     __syncthreads();
-    // after the barrier, which would otherwise wait for these stores to complete
-    if (write_new && last >= 0 && wave == 0 && g == 0)  // lanes 0 .. 15 copy the whole row
-        store_new_row<B, ROWB>(p, s, kvh, n, *reinterpret_cast<const u32x4 *>(nk), *reinterpret_cast<const u32x4 *>(nv));
 }
 
 // Per-item schedule: grid = (num_kv_heads, parts, num_seqs), block = 64 * W, the kv head fastest
@@ -336,7 +316,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         sink = Sink{p.ws + wr * 128, p.ws + p.ws_rows * 128 + wr, p.ws + p.ws_rows * 129 + wr,
                     static_cast<int64_t>(p.num_parts) * 128, p.num_parts};
     }
-    gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, t0, t1, sink, lds, t0 == 0);  // part 0 writes the new rows
+    gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, t0, t1, sink, lds);
 }
 
 // Balanced schedule: grid = balanced_wgs workgroups (one per CU), each an equal share of the
@@ -353,8 +333,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_zero_empty<E, 128, W * 64>(p, C);
     balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        // the share holding a row's first tile writes the new rows of a decode step
-        gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds, ta == 0);
+        gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
 }
 
