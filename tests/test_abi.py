@@ -89,6 +89,34 @@ def test_attention_rejects_bad_arguments(kw, code):
     assert _lib.load().pkv_last_error()
 
 
+def _step(**kw):
+    a = dict(out=FAKE, q=FAKE, nk=FAKE, nv=FAKE, slots=FAKE, k=FAKE, v=FAKE, num_blocks=10, tables=FAKE,
+             max_blocks=4, ctx=FAKE, max_ctx=64, S=2, hq=4, hkv=4, d=128, B=16, scale=0.1, P=0, ws=NULL, ws_bytes=0,
+             dtype=1, flags=0)
+    a.update(kw)
+    return _lib.load().pkv_paged_attention_decode_step(
+        a["out"], a["q"], a["nk"], a["nv"], a["slots"], a["k"], a["v"], a["num_blocks"], a["tables"], a["max_blocks"],
+        a["ctx"], a["max_ctx"], a["S"], a["hq"], a["hkv"], a["d"], a["B"], a["scale"], a["P"], a["ws"], a["ws_bytes"],
+        a["dtype"], a["flags"], NULL, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nk=NULL), _lib.PKV_EINVAL),
+    (dict(nv=NULL), _lib.PKV_EINVAL),
+    (dict(slots=NULL), _lib.PKV_EINVAL),
+    (dict(nk=ctypes.c_void_p((1 << 20) + 8)), _lib.PKV_EINVAL),  # misaligned new rows
+    (dict(B=12), _lib.PKV_EUNSUPPORTED),                            # the decode call's checks apply
+    (dict(P=24), _lib.PKV_EINVAL),
+])
+def test_step_rejects_bad_arguments(kw, code):
+    assert _step(**kw) == code
+    assert _lib.load().pkv_last_error()
+
+
+def test_step_with_no_sequences_is_a_no_op():
+    assert _step(S=0, out=NULL, q=NULL, nk=NULL, nv=NULL, slots=NULL) == _lib.PKV_OK
+
+
 def test_attention_with_no_sequences_is_a_no_op():
     assert _attn(S=0, out=NULL, q=NULL) == _lib.PKV_OK
 
