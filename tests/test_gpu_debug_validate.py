@@ -97,3 +97,32 @@ def test_reshape_and_cache_slots(monkeypatch):
     after[0, :, 5] = before[0, :, 5]
     after[1, :, 1] = before[1, :, 1]
     assert torch.equal(after, before)
+
+
+def _step(k, v, q, tables, ctx, slots, max_ctx=48):
+    out = torch.empty_like(q)
+    g = torch.Generator().manual_seed(11)
+    nk = (torch.randn(2, HKV, D, generator=g) * 0.5).half().to(q.device)
+    nv = (torch.randn(2, HKV, D, generator=g) * 0.5).half().to(q.device)
+    kernels.paged_attention_decode_step(out, q, nk, nv, slots, k, v, tables, ctx, max_ctx, D ** -0.5)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_step_slot_must_be_the_last_position(monkeypatch):
+    """The one-call step: each non-negative slot must be the slot of position length - 1 through
+    the table (sequence 0: length 20, its token 19 in block 1 at row 3; sequence 1: length 40,
+    token 39 in block 5 at row 7). A right slot and a negative one pass; any other is rejected
+    before anything is written."""
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    k, v, q, tables, ctx = _setup()
+    dev = q.device
+    good = torch.tensor([1 * B + 3, 5 * B + 7], dtype=torch.int64, device=dev)
+    _step(k, v, q, tables, ctx, good)
+    _step(k, v, q, tables, ctx, torch.tensor([-1, 5 * B + 7], dtype=torch.int64, device=dev))
+    k0, v0 = k.clone(), v.clone()
+    for bad in ([1 * B + 4, 5 * B + 7], [1 * B + 3, 6 * B + 7], [3 * B + 3, 5 * B + 7]):
+        _rejects(_step, k, v, q, tables, ctx, torch.tensor(bad, dtype=torch.int64, device=dev),
+                 match="slot_mapping")
+    assert torch.equal(k.view(torch.int16), k0.view(torch.int16)) and torch.equal(v.view(torch.int16),
+                                                                                   v0.view(torch.int16))
