@@ -172,53 +172,68 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 vf[u][i] = *reinterpret_cast<const u32x4 *>(&lds[b][1][u * TR + 4 * g + i][n * 16]);
+        // The row tiles' softmax runs phase by phase over all of them, with one branch per phase
+        // at most, so the tiles' independent chains share basic blocks and interleave.
+        float sc[RT][2][4], mloc[RT];
+        // a step wholly before a row tile's first row (and inside the pool) needs no mask; the
+        // tiles' first rows grow with the tile index, so the first tile's test covers them all
+        if ((t + 1) * kStepKeys - 1 <= qmin[0] && ok[0] && ok[1]) {  // uniform
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            float sc[2][4], mloc = -INFINITY;
-            // a step wholly before the tile's first row (and inside the pool) needs no mask
-            // (uniform: the rows' positions grow with the row index)
-            const bool open = (t + 1) * kStepKeys - 1 <= qmin[rt] && ok[0] && ok[1];
-            if (open) {
+            for (int rt = 0; rt < RT; ++rt) {
+                mloc[rt] = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        sc[u][i] = c[rt][u][i] * p.scale_log2;
-                        mloc = fmaxf(mloc, sc[u][i]);
+                        sc[rt][u][i] = c[rt][u][i] * p.scale_log2;
+                        mloc[rt] = fmaxf(mloc[rt], sc[rt][u][i]);
                     }
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                mloc[rt] = -INFINITY;
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int kpos = t * kStepKeys + u * TR + 4 * g + i;  // qpos < kend: kend is implied
-                        sc[u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
-                        mloc = fmaxf(mloc, sc[u][i]);
+                        sc[rt][u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
+                        mloc[rt] = fmaxf(mloc[rt], sc[rt][u][i]);
                     }
             }
-            mloc = max_over_lane_groups(mloc);
-            // m[rt] is the reference the weights are taken against, exp2(s - m). It moves to the
-            // running maximum only when some row's maximum passes it by more than kMaxSlack, so the
-            // rescale is rare; the weights stay below 2^kMaxSlack, and the quotient acc / l does not
-            // depend on the reference.
-            const float m_new = fmaxf(m[rt], mloc);
-            float m_ref;
-            if (__builtin_amdgcn_ballot_w64(m_new > m[rt] + kMaxSlack) != 0) {
-                m_ref = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fast_exp2(m[rt] - m_ref);
+        }
+        // m[rt] is the reference the weights are taken against, exp2(s - m). It moves to the
+        // running maximum only when some row's maximum passes it by more than kMaxSlack, so the
+        // rescale is rare; the weights stay below 2^kMaxSlack, and the quotient acc / l does not
+        // depend on the reference.
+        float m_new[RT];
+        bool grow = false;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            m_new[rt] = fmaxf(m[rt], max_over_lane_groups(mloc[rt]));
+            grow = grow || m_new[rt] > m[rt] + kMaxSlack;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float ref = m_new[rt] == -INFINITY ? 0.f : m_new[rt];
+                const float alpha = fast_exp2(m[rt] - ref);
                 lsum[rt] *= alpha;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[rt][j] *= alpha;
-                m[rt] = m_new;
-            } else {
-                m_ref = m[rt] == -INFINITY ? 0.f : m[rt];
+                m[rt] = m_new[rt];
             }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float m_ref = m[rt] == -INFINITY ? 0.f : m[rt];
             unsigned h[4], r[4];  // weights of keys (u, 2w), (u, 2w + 1) in word 2u + w
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    const float e0 = fast_exp2(sc[u][2 * w] - m_ref), e1 = fast_exp2(sc[u][2 * w + 1] - m_ref);
+                    const float e0 = fast_exp2(sc[rt][u][2 * w] - m_ref), e1 = fast_exp2(sc[rt][u][2 * w + 1] - m_ref);
                     const unsigned hw = M::pack2(e0, e1);
                     h[2 * u + w] = hw;
                     r[2 * u + w] = M::pack2(e0 - M::value(hw & 0xffffu), e1 - M::value(hw >> 16));
