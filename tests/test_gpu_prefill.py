@@ -65,8 +65,8 @@ def test_prefill_over_prefix_cache_blocks():
 
 
 def test_prefill_negative_scale():
-    """A negative scale (the kernel takes its magnitude and flips the queries' sign bits) gives
-    the oracle's result for that scale."""
+    """A negative scale gives the oracle's result for that scale (the kernel scales the logits
+    before it takes their running maximum, so the sign needs no special case)."""
     w = CASES["gqa-bf16-g4-b16"]()
     w.scale = -w.scale
     out, ref, n = _prefill_case(w, lambda c: min(c, 1 + c // 3), seed=17)
