@@ -32,6 +32,9 @@ CASES = {
                                                       dtype="f16", partition_size=256),
     "gqa-f16-g8-b32": lambda: synth.gqa_shared_prefix(num_seqs=5, prefix=48, median=150, cap=700, hq=16, hkv=2,
                                                       d=128, block_size=32, dtype="f16", partition_size=256),
+    # the timed configurations at their full sizes (the step call is what the bench times)
+    "13b-full": lambda: synth.llama13b(),
+    "gqa-full": lambda: synth.gqa_shared_prefix(),
 }
 
 
@@ -55,7 +58,7 @@ def _state(w):
     return c, new_k, new_v, torch.from_numpy(slots).cuda()
 
 
-@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("name", [pytest.param(n, marks=pytest.mark.full) if n.endswith("-full") else n for n in CASES])
 def test_step_equals_cache_write_then_attention(name):
     w = CASES[name]()
     st = oracle.replay(w)
