@@ -450,7 +450,7 @@ def memory_sim_leg(seed=7, block_size=16, reserve=2048, oracle_requests=400):
     import synth
     from oracle import simulator as ref
     from paged_kv_cache_416_amd import sim
-    configs = []
+    budgets = []
     for name, kv_bytes, n, max_batch in (("40GB-device-13B", 0.30 * 40e9, 2000, 256),
                                          ("mi355x-288GB-13B", 288e9 - 26e9 - 10e9, 20000, 4096)):
         blocks = int(kv_bytes // (KV_TOKEN_BYTES_13B * block_size))
@@ -472,9 +472,9 @@ def memory_sim_leg(seed=7, block_size=16, reserve=2048, oracle_requests=400):
             summary = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in summary.items()}
             summary["native_us_per_step"] = round(1e6 * dt / len(trace), 2)
             entry[kind] = summary
-        configs.append(entry)
+        budgets.append(entry)
     # the oracle beside the native simulator, on the first requests of the first budget
-    c = configs[0]
+    c = budgets[0]
     a, p, o = synth.serving_requests(seed, c["requests"], 160, 200, 1.0, reserve, None)
     a, p, o = a[:oracle_requests], p[:oracle_requests], o[:oracle_requests]
     args = (c["slots"] // block_size, block_size, c["watermark_blocks"], c["max_batch"], a, p, o)
@@ -487,7 +487,7 @@ def memory_sim_leg(seed=7, block_size=16, reserve=2048, oracle_requests=400):
     return {"metric": "continuous-batching memory simulator: useful share of held KV memory, paged vs contiguous "
                       "reservation",
             "data": "synthetic (seeded log-normal prompt/output lengths, all requests waiting at step 0)",
-            "configs": configs,
+            "budgets": budgets,
             "oracle": {"sample": f"paged scheme, first {oracle_requests} requests of {c['workload']}",
                        "steps": len(rows), "native_ms": round(1e3 * t_nat, 2), "oracle_ms": round(1e3 * t_ref, 1),
                        "identical": bool(np.array_equal(nat, np.array(rows, dtype=np.int64)))}}
