@@ -523,8 +523,9 @@ def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=10):
     flops = 4 * d * hq * seqs * prompt_len * (prompt_len + 1) / 2
     tf = flops / (us * 1e-6) / 1e12
     return {"sequences": seqs, "prompt_len": prompt_len, "q_heads": hq, "kv_heads": hkv, "dtype": "bf16",
-            "us": round(us, 1), "TFLOP/s": round(tf, 1), "roofline": {"bound": "mfma", "peak": 2500.0,
-                                                                       "frac": round(tf / 2500.0, 4)},
+            "us": round(us, 1), "TFLOP/s": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tf / 2500.0, 4), "traffic": None},
             "tokens_per_s": round(seqs * prompt_len / (us * 1e-6), 0)}
 
 
