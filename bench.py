@@ -493,7 +493,7 @@ def memory_sim_leg(seed=7, block_size=16, reserve=2048, oracle_requests=400):
                        "identical": bool(np.array_equal(nat, np.array(rows, dtype=np.int64)))}}
 
 
-def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=10):
+def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=30, warmup=100):
     """Paged prefill at the 8B shape: `seqs` fresh prompts of `prompt_len` tokens, every token a
     causal query over the paged cache (random placement). Algorithmic flops: 4 d per (query,
     visible key, query head): q.k and p.v."""
@@ -517,7 +517,9 @@ def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=10):
     def run(i):
         kernels.paged_attention_prefill(out, q, k, v, tables, ctx, qs, prompt_len, prompt_len, d ** -0.5)
 
-    for i in range(3):
+    # a long warm-up: after the decode legs' host-side work the first tens of launches run up to
+    # 8 % slow while the device returns to its steady clocks
+    for i in range(warmup):
         run(i)
     us = timed_launches(run, reps, stream)
     flops = 4 * d * hq * seqs * prompt_len * (prompt_len + 1) / 2

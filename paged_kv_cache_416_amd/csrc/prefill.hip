@@ -140,12 +140,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int u = 0; u < 2; ++u) cp[u] = trow[min(ct * kStepKeys + u * TR, kend - 1) / B];
     };
 
-    float m[RT], lsum[RT];
+    float m[RT];
+    const unsigned one2 = M::pack2(1.f, 1.f);
+    const u32x4 kOnes = {one2, one2, one2, one2};
+    f32x4 lsum[RT];  // row n's weight sum in every element of lane (n, g): the all-ones product
     f32x4 acc[RT][8];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         m[rt] = -INFINITY;
-        lsum[rt] = 0.f;
+        lsum[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -219,7 +222,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int rt = 0; rt < RT; ++rt) {
                 const float ref = m_new[rt] == -INFINITY ? 0.f : m_new[rt];
                 const float alpha = fast_exp2(m[rt] - ref);
-                lsum[rt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lsum[rt][i] *= alpha;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[rt][j] *= alpha;
                 m[rt] = m_new[rt];
@@ -238,12 +242,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                     h[2 * u + w] = hw;
                     r[2 * u + w] = M::pack2(e0 - M::value(hw & 0xffffu), e1 - M::value(hw >> 16));
                 }
-            float l = lsum[rt];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) l = M::sum2(h[w], l);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) l = M::sum2(r[w], l);
-            lsum[rt] = l;
             const u32x4 ph = {h[0], h[1], h[2], h[3]}, pr = {r[0], r[1], r[2], r[3]};
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -255,6 +253,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                                   __builtin_amdgcn_perm(word(vf[1][3], w), word(vf[1][2], w), sel)};
                 acc[rt][j] = M::mma(vt, pr, M::mma(vt, ph, acc[rt][j]));
             }
+            // the weight sums on the matrix cores: an all-ones operand in place of V^T gives
+            // every row of the product the column sum of P^T, the same fp32 accumulation
+            lsum[rt] = M::mma(kOnes, pr, M::mma(kOnes, ph, lsum[rt]));
         }
     };
 
@@ -293,12 +294,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         step(R[1], 1);
     }
 
-    // each row's weight sum over the four lane groups; lane (n, g) holds d = 8 (4g + i) + j
+    // lane (n, g) holds row n's weight sum and d = 8 (4g + i) + j of its output
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-        float l = lsum[rt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = lsum[rt][0];
         if (row_ok[rt]) {
             const float inv = l > 0.f ? 1.f / l : 0.f;
             const int64_t base = (static_cast<int64_t>(q0 + tok[rt]) * p.num_q_heads + head[rt]) * D;
