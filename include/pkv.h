@@ -78,8 +78,8 @@ const char *pkv_version(void);
  * ==================================================================== */
 typedef struct pkv_pool pkv_pool;
 
-/* One pool of num_blocks physical blocks of block_size tokens ("one pool instead
- * of private reserves", slide 12). free_order (host, nullable) is a permutation of
+/* One pool of num_blocks physical blocks of block_size tokens (slide 12: a single
+ * shared pool takes the place of per-request reservations). free_order (host, nullable) is a permutation of
  * 0..num_blocks-1: the order in which free blocks are handed out (NULL = ascending).
  * Free blocks form a LIFO stack: a freed block is the next one handed out. */
 int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order, pkv_pool **out);
@@ -97,7 +97,7 @@ int pkv_seq_add(pkv_pool *pool, int64_t seq_id);
  * their blocks immediately). */
 int pkv_seq_free(pkv_pool *pool, int64_t seq_id);
 /* child shares all of parent's blocks: same table and length, every block's count + 1
- * (slide 14; lesson note section 3: ref_count <- ref_count + 1). */
+ * (slide 14; lesson note section 3: sharing raises a block's count by one). */
 int pkv_seq_fork(pkv_pool *pool, int64_t parent, int64_t child);
 /* Length in tokens (>= 0), or PKV_ENOSEQ. */
 int64_t pkv_seq_len(const pkv_pool *pool, int64_t seq_id);
@@ -112,7 +112,8 @@ int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32
  *  - A block is taken only when the last one is full (slide 11).
  *  - If a sequence's last block is shared (count > 1) and partly filled, the sequence
  *    first gets a private copy: a new block dst, the pair (src, dst) is emitted, src's
- *    count drops by one (slide 13: only the last block is ever copied). The last sharer
+ *    count drops by one (slide 13: copy-on-write duplicates the shared last block and
+ *    nothing else). The last sharer
  *    left writes in place, so n sharers make n-1 copies.
  * Sequences are served in the order given; a sequence may appear once per call.
  * slots_out (host, int64[sum n_tokens]) receives the slots in request order;
@@ -123,9 +124,9 @@ int32_t pkv_seq_blocks(const pkv_pool *pool, int64_t seq_id, int32_t *out, int32
 int pkv_seq_append(pkv_pool *pool, const int64_t *seq_ids, const int32_t *n_tokens, int32_t n_seqs,
                    int64_t *slots_out, int32_t *cow_pairs_out, int32_t max_pairs, int32_t *n_pairs_out);
 
-/* Prefix cache (the lesson note, section 3.1: hundreds of requests share one system prompt; a
- * cryptographic hash of each prompt block finds existing blocks, which the new request maps,
- * incrementing their counts, so their keys and values are not computed again).
+/* Prefix cache (the lesson note, section 3.1: when many requests open with the same system
+ * prompt, a cryptographic digest per prompt block finds blocks the pool already holds; the new
+ * request maps them and raises their counts, and their keys and values are not computed again).
  * Digest of full prompt block j: SHA-256 of (digest of block j-1, or 32 zero bytes for j = 0)
  * followed by the block's block_size token ids as little-endian int32: equal digests mean
  * equal prefixes. Only full prompt blocks are hashed. A hashed block that falls free keeps its
@@ -243,13 +244,13 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_context_len, int32_t partition_size);
 
 /* Decode attention over the paged cache, one query token per sequence (slide 9: attention
- * block by block; keys and values fetched from non-contiguous blocks by address):
+ * evaluated one block at a time, keys and values read from physically scattered blocks):
  *   for each sequence s and query head h (kv head h / (num_q_heads/num_kv_heads)):
  *   out[s][h] = softmax_t(scale * q[s][h] . K_t) . V_t over t < context_lens[s],
  *   K_t, V_t read from block block_tables[s][t / block_size], row t % block_size.
  *  out, q:        [num_seqs][num_q_heads][head_dim]; out is written in dtype (RNE).
  *  block_tables:  device int32[num_seqs][max_blocks_per_seq]; entries past a sequence's
- *                 last block are never read.
+ *                 last block are never read (so they may hold anything).
  *  context_lens:  device int32[num_seqs]; a sequence with length 0 gets zeros.
  *  max_context_len: host bound on context_lens, sizes the launch.
  *  partition_size: 0 = one pass per (sequence, head). > 0 (a multiple of block_size):
@@ -303,8 +304,11 @@ int pkv_paged_attention_decode(void *out, const void *q, const void *k_cache, co
  *                 so its slot must be negative.
  *  k_cache, v_cache: written at those slots (one row per kv head) and read.
  *  everything else: as for pkv_paged_attention_decode.
- * In one launch, attention takes each sequence's last row from new_k/new_v rather than reading it
- * back from the cache, so nothing in the launch reads what it writes. A slot that is not the slot of position
+ * In one launch, attention takes each sequence's last row from new_k/new_v rather than from the
+ * cache: no value the launch computes with comes from a location it writes. (The lanes of that row
+ * still issue their load of its old cache bytes, which may race with the row's store by another
+ * workgroup; a select replaces the loaded value before any arithmetic, so the race cannot reach a
+ * result.) A slot that is not the slot of position
  * context_lens[s] - 1 is a caller error (the results then differ from the two calls);
  * PKV_DEBUG_VALIDATE=1 reports it as PKV_EINVAL, with the checks of the decode call. */
 int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k, const void *new_v,
@@ -322,22 +326,27 @@ int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k,
  * slides 9 and 10: keys and values fetched block by block through the block table). The
  * queries' own keys and values must already be in the cache (pkv_reshape_and_cache).
  *   out[r][h] = softmax_t(scale * q[r][h] . K_t) . V_t over t <= p, for row r = query_start[s] + i
- *  out, q: [query_start[num_seqs]][num_q_heads][head_dim], dtype, out written with RNE.
- *  query_start: device int32[num_seqs + 1], query_start[0] = 0, non-decreasing;
- *               n_s <= context_lens[s]; max_query_len: host bound on n_s (sizes the launch).
+ *  out, q: [num_tokens][num_q_heads][head_dim], dtype, out written with RNE; rows past
+ *          query_start[num_seqs] are not touched.
+ *  query_start: device int32[num_seqs + 1], query_start[0] = 0, non-decreasing,
+ *               query_start[num_seqs] <= num_tokens; n_s <= context_lens[s].
+ *  num_tokens: rows of q and out (>= 0). max_query_len: host bound on n_s (sizes the launch).
  *  block_tables, context_lens, max_context_len, scale: as for pkv_paged_attention_decode.
  *  flags: 0.
  * The grouped-query matrix-core kernel generalised: a wave owns 16 (query token, query head)
  * rows of one kv head and walks every key tile up to its last row's position.
  * Supported: f16/bf16, head_dim 128, block_size 16 or 32, num_q_heads a multiple of
- * num_kv_heads. A sequence with n_s > context_lens[s] gets no output (a caller error;
- * PKV_DEBUG_VALIDATE=1 reports it, with the checks of the decode call, as PKV_EINVAL). */
+ * num_kv_heads. Device-side guards (caller errors; never a fault, but that sequence gets no
+ * output): a sequence with n_s > context_lens[s], or whose rows query_start[s] ..
+ * query_start[s+1] - 1 do not lie inside [0, num_tokens). PKV_DEBUG_VALIDATE=1 reports these,
+ * query_start[0] != 0 and n_s > max_query_len as PKV_EINVAL, with the checks of the decode call
+ * (query_start and context_lens copied to the host, synchronising the stream). */
 int pkv_paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                                 int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                const int32_t *context_lens, const int32_t *query_start, int32_t max_query_len,
-                                int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, float scale, int32_t dtype, uint32_t flags,
-                                hipStream_t stream);
+                                const int32_t *context_lens, const int32_t *query_start, int32_t num_tokens,
+                                int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                float scale, int32_t dtype, uint32_t flags, hipStream_t stream);
 
 /* The same attention over a contiguous cache, the layout paging replaces (slide 19 prices
  * the indirection against it): k, v are [num_seqs][num_kv_heads][lmax][head_dim] and token t

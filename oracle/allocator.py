@@ -1,15 +1,15 @@
 """Reference model of the block-pool allocator -- TEST INFRASTRUCTURE ONLY (pure Python).
 
 Follows the pages' statement of the problem:
-  * one pool of fixed-size physical blocks; any free block serves any request
-    ("vLLM and PagedAttention" slides, slide 12, and the "Week 22 Day 2"
-    lesson note, section 2: any free block can satisfy any request);
+  * one pool of fixed-size physical blocks, and a request may take whichever
+    block is free ("vLLM and PagedAttention" slides, slide 12, and the "Week 22
+    Day 2" lesson note, section 2);
   * a per-sequence block table maps logical block j (tokens j*B .. j*B+B-1) to
     a physical block (slide 10; lesson note section 2, block-table diagram);
   * a new block is taken only when the last one is full (slide 11);
   * sharing increments a block's reference count (lesson note section 3.1);
   * a sequence about to write into a shared, partly filled last block gets a
-    private copy first; only the last block is ever copied (slide 13, lesson
+    private copy first, and no other block is ever duplicated (slide 13, lesson
     note section 3.2);
   * finished sequences return their blocks at once (lesson note section 4);
   * a request that cannot get all its blocks gets none (slide 15).
@@ -22,9 +22,9 @@ same choices independently):
   * within one batched append, sequences are served in the order given, and
     the whole batch fails, changing nothing, if the pool runs short.
 
-Prefix cache (lesson note section 3.1: a cryptographic hash of each prompt block;
-a new request whose block hashes to an existing block maps it and increments its
-count). Readings: the digest of full prompt block j is SHA-256 (Python's hashlib)
+Prefix cache (lesson note section 3.1: prompt blocks are looked up by a
+cryptographic digest; a new request whose block has the digest of a held block
+maps that block and increments its count). Readings: the digest of full prompt block j is SHA-256 (Python's hashlib)
 of the previous block's digest (32 zero bytes for the first) followed by the
 block's token ids as little-endian int32, so equal digests mean equal prefixes;
 only full prompt blocks are hashed and hits are taken as a prefix of the prompt; a

@@ -8,9 +8,10 @@
  * Everything here is the plain definition, written out:
  *   - key/value cache writes are byte copies of a token's rows into the slot
  *     the block table gives it ("vLLM and PagedAttention" slides, slide 11:
- *     a new token goes into the free slot of the last block);
- *   - block copies are whole-block memcpy ("Parallel samples: copy on write",
- *     slide 13; only the last block is ever copied);
+ *     a new token lands in the next free slot of its sequence's last block);
+ *   - block copies are whole-block memcpy (slide 13 of the same deck, on
+ *     sampling several outputs from one prompt: copy-on-write duplicates a
+ *     shared last block only);
  *   - attention is single-query scaled dot-product attention over the keys
  *     and values gathered through the block table ("PagedAttention: attention
  *     block by block", slide 9: where the bytes come from changes, not what is
@@ -269,6 +270,13 @@ int oracle_paged_attention(double *out, const void *q, const void *k_cache, cons
                 double M = -INFINITY;
                 double *ms = (double *)malloc(sizeof(double) * 2 * nparts);
                 double *os = (double *)malloc(sizeof(double) * nparts * head_dim);
+                if (!ms || !os) {
+                    free(ms);
+                    free(os);
+#pragma omp atomic write
+                    err = ORC_ENOMEM;
+                    continue;
+                }
                 for (int64_t p = 0; p < nparts; ++p) {
                     int64_t t0 = p * partition_size, t1 = t0 + partition_size < ctx ? t0 + partition_size : ctx;
                     attend_one(os + p * head_dim, q, q_off, k_cache, v_cache, paged_row, &rc, t0, t1,

@@ -6,10 +6,10 @@ waiting requests are admitted and prefilled into the running batch) under two sc
 hold the same number of token slots:
 
   * paged: the block pool of ``oracle.allocator`` (slides 10-12: fixed-size blocks from one
-    pool, a new block only when the last one is full); when a decode step cannot get its
-    blocks, the newest running request is evicted whole and waits again at the head of the
-    queue (slide 15: first come first served, the newest request is evicted, all or nothing;
-    recovery by recompute);
+    pool, a block allocated only once the last one has no free slot); when a decode step
+    cannot get its blocks, the newest running request is evicted whole and waits again at the
+    head of the queue (slide 15: requests are served in arrival order, and under memory
+    pressure the latest arrival leaves entirely; it comes back by recomputation);
   * contiguous: each admitted request reserves one contiguous run of ``reserve`` slots, placed
     first-fit in a linear address space and released on finish (the lesson note, section 1:
     reservation for the maximum length, and holes left by requests that finish at different

@@ -1,8 +1,8 @@
 // Decode attention over a paged KV cache, one query token per sequence.
 //
-// "vLLM and PagedAttention" slide 9: attention is computed block by block;
-// keys and values are fetched from non-contiguous blocks by address, through
-// the block table (slide 10). The result is ordinary single-query scaled
+// "vLLM and PagedAttention" slide 9: attention is evaluated one block at a
+// time, with keys and values read from physically scattered blocks located
+// through the block table (slide 10). The result is ordinary single-query scaled
 // dot-product attention over the sequence's gathered context.
 //
 // Kernel design (gfx950, wave64), one workgroup of W waves per
@@ -86,13 +86,15 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
     // this wave takes tiles jt0 + wave + k*W, k = 0 .. nk-1, in stages of U tiles.
     const int jt0 = t0 / TR;
 
-    // Block-table chunk: lane i holds the physical block of this wave's tile kc0 + i; entries
-    // past the sequence's last block are read but never used.
+    // Block-table chunk: lane i holds the physical block of this wave's tile kc0 + i. A lane whose
+    // tile lies past the range's last block (t1 <= the length) reads no entry and holds 0, which
+    // no tile uses.
     const int32_t *trow = PAGED ? p.tables + static_cast<int64_t>(s) * p.max_blocks : nullptr;
+    const int jlast = (t1 - 1) / B;  // the range's last block (< max_blocks: t1 <= ctx_cap)
     int tb = 0;
     auto fetch_table = [&](int base) -> int {
         const int j = (jt0 + wave + (base + lane) * W) / SPB;
-        return j < p.max_blocks ? trow[j] : 0;
+        return j <= jlast ? trow[j] : 0;
     };
     if constexpr (PAGED) tb = fetch_table(0);
     // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)

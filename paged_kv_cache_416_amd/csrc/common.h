@@ -42,10 +42,10 @@ int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_
                        const int32_t *block_tables, int32_t max_blocks, int32_t block_size, int64_t num_blocks,
                        int32_t lmax, hipStream_t stream);
 
-// query_start[0] = 0 and each sequence's query count in [0, min(max_query_len, its length)].
-// Synchronises `stream`.
+// query_start[0] = 0, each sequence's query count in [0, min(max_query_len, its length)] and
+// query_start[num_seqs] <= num_tokens. Synchronises `stream`.
 int validate_query_start(const char *fn, const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,
-                         int32_t max_query_len, hipStream_t stream);
+                         int32_t num_tokens, int32_t max_query_len, hipStream_t stream);
 
 // Slots below num_slots and no non-negative slot twice. Synchronises `stream`.
 int validate_slots(const char *fn, const int64_t *slot_mapping, int32_t num_tokens, int64_t num_slots,

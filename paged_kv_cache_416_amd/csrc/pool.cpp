@@ -2,7 +2,7 @@
 //
 // "vLLM and PagedAttention" slides 10-16 and the "Week 22 Day 2" lesson note,
 // sections 2-4: one pool of fixed-size blocks shared by all requests, a
-// per-sequence block table, a new block only when the last one is full,
+// per-sequence block table, allocation only once the last block has no free slot,
 // reference-counted sharing (fork), copy-on-write of a shared, partly filled
 // last block, immediate release of a finished sequence's blocks, and
 // all-or-nothing admission when the pool runs short.
@@ -12,9 +12,9 @@
 // sequence returns its blocks in logical order; a batched append serves its
 // sequences in the order given.
 //
-// Prefix cache (the lesson note, section 3.1: a cryptographic hash of each prompt block; a new
-// request whose prompt block hashes to an existing block maps that block and increments its
-// count). Readings: the digest of full prompt block j is SHA-256 of (the digest of block j-1,
+// Prefix cache (the lesson note, section 3.1: prompt blocks are looked up by a cryptographic
+// digest; a new request whose prompt block has the digest of a held block maps that block and
+// increments its count). Readings: the digest of full prompt block j is SHA-256 of (the digest of block j-1,
 // or 32 zero bytes for j = 0) followed by the block's token ids as little-endian int32, so equal
 // digests mean equal prefixes, which is what a block's keys and values depend on; only full
 // prompt blocks are hashed, and hits are taken as a prefix of the prompt. A hashed block that

@@ -34,7 +34,7 @@ struct PrefillParams {
     const void *q, *k, *v;
     const int32_t *tables, *ctx_lens, *query_start;
     uint32_t num_blocks;
-    int32_t max_blocks, ctx_cap, num_q_heads, num_kv_heads, group;
+    int32_t num_tokens, max_blocks, ctx_cap, num_q_heads, num_kv_heads, group;
     float scale_log2;
 };
 
@@ -62,7 +62,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int ctx = clamp_ctx(__builtin_amdgcn_readfirstlane(p.ctx_lens[s]), p.ctx_cap);
     const int rows = nq * G;
     const int wg_row0 = (gridDim.x - 1 - blockIdx.x) * W * RT * 16;
-    if (nq <= 0 || nq > ctx || wg_row0 >= rows) return;  // uniform over the workgroup
+    // uniform over the workgroup; a sequence whose rows are not all inside q and out is skipped
+    if (nq <= 0 || nq > ctx || q0 < 0 || q0 > p.num_tokens - nq || wg_row0 >= rows) return;
     const int row0 = wg_row0 + wave * RT * 16;  // a wave past the last row still loads and waits
 
     // row n of each of the wave's row tiles: query token, head, position
@@ -328,13 +329,14 @@ using namespace pkv;
 extern "C" int pkv_paged_attention_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
                                            int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
                                            const int32_t *context_lens, const int32_t *query_start,
-                                           int32_t max_query_len, int32_t max_context_len, int32_t num_seqs,
-                                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                           int32_t block_size, float scale, int32_t dtype, uint32_t flags,
-                                           hipStream_t stream) {
+                                           int32_t num_tokens, int32_t max_query_len, int32_t max_context_len,
+                                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, float scale, int32_t dtype,
+                                           uint32_t flags, hipStream_t stream) {
     const char *fn = "pkv_paged_attention_prefill";
     if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "%s: num_seqs %d outside [0, 65535]", fn, num_seqs);
-    if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+    if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens %d < 0", fn, num_tokens);
+    if (num_seqs == 0 || max_query_len == 0 || num_tokens == 0) return PKV_OK;
     if (dtype != PKV_F16 && dtype != PKV_BF16)
         return fail(PKV_EUNSUPPORTED, "%s: dtype %d not built (f16, bf16)", fn, dtype);
     if (head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d not built (128)", fn, head_dim);
@@ -356,7 +358,7 @@ extern "C" int pkv_paged_attention_prefill(void *out, const void *q, const void 
         int rc = validate_attention(fn, context_lens, num_seqs, max_context_len, block_tables, max_blocks_per_seq,
                                     block_size, num_blocks, 0, stream);
         if (rc) return rc;
-        rc = validate_query_start(fn, query_start, context_lens, num_seqs, max_query_len, stream);
+        rc = validate_query_start(fn, query_start, context_lens, num_seqs, num_tokens, max_query_len, stream);
         if (rc) return rc;
     }
     PrefillParams p{};
@@ -368,6 +370,7 @@ extern "C" int pkv_paged_attention_prefill(void *out, const void *q, const void 
     p.ctx_lens = context_lens;
     p.query_start = query_start;
     p.num_blocks = static_cast<uint32_t>(num_blocks);
+    p.num_tokens = num_tokens;
     p.max_blocks = max_blocks_per_seq;
     p.ctx_cap = static_cast<int32_t>(
         std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));

@@ -1,5 +1,5 @@
 // SHA-256 (FIPS 180-4, sections 4.1.2, 5.1.1, 6.2) for the prefix cache's block digests: the
-// lesson note "Week 22 Day 2", section 3.1, names a cryptographic hash of each prompt block.
+// lesson note "Week 22 Day 2", section 3.1, identifies prompt blocks by a cryptographic digest.
 // The round constants and the initial hash value are computed from their definition (the first
 // 32 bits of the fractional parts of the cube roots of the first 64 primes, and of the square
 // roots of the first 8 primes) rather than typed in.

@@ -103,7 +103,7 @@ int validate_attention(const char *fn, const int32_t *context_lens, int32_t num_
 }
 
 int validate_query_start(const char *fn, const int32_t *query_start, const int32_t *context_lens, int32_t num_seqs,
-                         int32_t max_query_len, hipStream_t stream) {
+                         int32_t num_tokens, int32_t max_query_len, hipStream_t stream) {
     std::vector<int32_t> qs, ctx;
     int rc = fetch(fn, "query_start", query_start, static_cast<size_t>(num_seqs) + 1, stream, qs);
     if (rc) return rc;
@@ -117,6 +117,9 @@ int validate_query_start(const char *fn, const int32_t *query_start, const int32
                         "%s: sequence %d has %d queries (max_query_len %d, context %d) (PKV_DEBUG_VALIDATE)", fn, s, n,
                         max_query_len, ctx[s]);
     }
+    if (qs[num_seqs] > num_tokens)
+        return fail(PKV_EINVAL, "%s: query_start[%d] = %d exceeds num_tokens %d (PKV_DEBUG_VALIDATE)", fn, num_seqs,
+                    qs[num_seqs], num_tokens);
     return PKV_OK;
 }
 

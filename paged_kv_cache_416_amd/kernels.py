@@ -204,13 +204,16 @@ def read_probe(src, sink):
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len,
                             max_context_len, scale, flags=0):
     """out/q [T, Hq, D] (rows query_start[s]..query_start[s+1]-1 are sequence s's last queries, causal);
-    caches [N, Hkv, B, D]; block_tables int32 [S, max_blocks]; context_lens int32 [S]; query_start int32 [S+1]."""
-    _need_cuda(out, q, k_cache, v_cache, block_tables, context_lens, query_start)
+    caches [N, Hkv, B, D]; block_tables int32 [S, max_blocks]; context_lens int32 [S]; query_start int32 [S+1]
+    with query_start[S] <= T (the library bounds the rows by T on the device)."""
     T, hq, d = q.shape
     N, hkv, B, d2 = k_cache.shape
     S = context_lens.shape[0]
     if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape or query_start.shape != (S + 1,):
         raise ValueError("shape mismatch")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError(f"block_tables must be [S={S}, max_blocks], got {tuple(block_tables.shape)}")
+    _need_cuda(out, q, k_cache, v_cache, block_tables, context_lens, query_start)
     for t in (out, q, k_cache, v_cache, block_tables, context_lens, query_start):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
@@ -219,7 +222,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start.dtype != torch.int32:
         raise ValueError("tables, lengths and query_start must be int32")
     check(load().pkv_paged_attention_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N, _ptr(block_tables),
-                                             block_tables.shape[1], _ptr(context_lens), _ptr(query_start),
+                                             block_tables.shape[1], _ptr(context_lens), _ptr(query_start), T,
                                              int(max_query_len), int(max_context_len), S, hq, hkv, d, B, float(scale),
                                              dtype_code(q.dtype), int(flags), _stream()))
     return out

@@ -210,3 +210,49 @@ def test_swap_blocks_host_validation():
     # fake addresses are neither device nor pinned host memory: refused before any launch
     assert call([0, 1]) == _lib.PKV_EINVAL
     assert b"pinned" in lib.pkv_last_error()
+
+
+def _prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, num_blocks=10, tables=FAKE, max_blocks=4, ctx=FAKE, qs=FAKE, T=8,
+             max_q=4, max_ctx=64, S=2, hq=8, hkv=2, d=128, B=16, scale=0.1, dtype=2, flags=0)
+    a.update(kw)
+    return _lib.load().pkv_paged_attention_prefill(a["out"], a["q"], a["k"], a["v"], a["num_blocks"], a["tables"],
+                                                   a["max_blocks"], a["ctx"], a["qs"], a["T"], a["max_q"],
+                                                   a["max_ctx"], a["S"], a["hq"], a["hkv"], a["d"], a["B"],
+                                                   a["scale"], a["dtype"], a["flags"], NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), _lib.PKV_EINVAL),              # rows of q and out
+    (dict(dtype=0), _lib.PKV_EUNSUPPORTED),     # fp32 has no matrix-core build
+    (dict(d=64), _lib.PKV_EUNSUPPORTED),
+    (dict(B=8), _lib.PKV_EUNSUPPORTED),
+    (dict(hq=6, hkv=4), _lib.PKV_EINVAL),
+    (dict(flags=1), _lib.PKV_EINVAL),
+    (dict(qs=NULL), _lib.PKV_EINVAL),
+    (dict(q=ctypes.c_void_p((1 << 20) + 8)), _lib.PKV_EINVAL),
+    (dict(scale=float("inf")), _lib.PKV_EINVAL),
+    (dict(max_blocks=0), _lib.PKV_EINVAL),
+])
+def test_prefill_rejects_bad_arguments(kw, code):
+    assert _prefill(**kw) == code
+    assert _lib.load().pkv_last_error()
+
+
+def test_prefill_with_no_rows_is_a_no_op():
+    assert _prefill(T=0, out=NULL, q=NULL) == _lib.PKV_OK
+    assert _prefill(S=0, out=NULL, q=NULL) == _lib.PKV_OK
+
+
+def test_prefill_wrapper_checks_the_table_shape():
+    """The binding rejects a block table whose rows do not match the sequences before anything
+    reaches the library (CPU tensors: the shape check comes first)."""
+    torch = pytest.importorskip("torch")
+    from paged_kv_cache_416_amd import kernels
+    q = torch.zeros(6, 8, 128, dtype=torch.bfloat16)
+    k = torch.zeros(4, 2, 16, 128, dtype=torch.bfloat16)
+    ctx = torch.tensor([3, 3], dtype=torch.int32)
+    qs = torch.tensor([0, 3, 6], dtype=torch.int32)
+    for bad in (torch.zeros(3, 2, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)):
+        with pytest.raises(ValueError, match="block_tables"):
+            kernels.paged_attention_prefill(torch.empty_like(q), q, k, k, bad, ctx, qs, 3, 3, 0.1)

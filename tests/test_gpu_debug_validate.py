@@ -126,3 +126,35 @@ def test_step_slot_must_be_the_last_position(monkeypatch):
                  match="slot_mapping")
     assert torch.equal(k.view(torch.int16), k0.view(torch.int16)) and torch.equal(v.view(torch.int16),
                                                                                    v0.view(torch.int16))
+
+
+def test_prefill_rows_bounded_by_num_tokens(monkeypatch):
+    """Prefill: the rows of q and out are num_tokens (the wrapper passes q.shape[0]). A query_start
+    whose last entry lies past them is rejected with PKV_DEBUG_VALIDATE; without the check the
+    kernel's own guard skips that sequence, and no row of out outside the valid sequences is
+    written."""
+    g = torch.Generator().manual_seed(3)
+    dev = torch.device("cuda")
+    d = 128
+    k = (torch.randn(4, HKV, B, d, generator=g) * 0.5).half().to(dev)
+    v = (torch.randn(4, HKV, B, d, generator=g) * 0.5).half().to(dev)
+    q = (torch.randn(10, HQ, d, generator=g) * 0.5).half().to(dev)
+    tables = torch.tensor([[0, 1], [2, 3]], dtype=torch.int32, device=dev)
+    ctx = torch.tensor([20, 32], dtype=torch.int32, device=dev)
+
+    def run(qs, max_q):
+        out = torch.full_like(q, float("nan"))
+        kernels.paged_attention_prefill(out, q, k, v, tables, ctx, torch.tensor(qs, dtype=torch.int32, device=dev),
+                                        max_q, 32, d ** -0.5)
+        torch.cuda.synchronize()
+        return out
+
+    plain = run([0, 4, 10], 6)
+    assert not torch.isnan(plain).any()
+    # sequence 1 claims rows 4 .. 11 of a 10-row q
+    bad = run([0, 4, 12], 8)
+    assert torch.equal(bad[:4].view(torch.int16), plain[:4].view(torch.int16))
+    assert torch.isnan(bad[4:]).all()
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    assert torch.equal(run([0, 4, 10], 6).view(torch.int16), plain.view(torch.int16))
+    _rejects(run, [0, 4, 12], 8, match="exceeds num_tokens")

@@ -1,6 +1,8 @@
 """Paged prefill (chunked, causal) through the C ABI against the oracle: each sequence's last n_s
 tokens are queries over its whole context (earlier chunks and shared prefix blocks included),
 n_s from 0 to the whole context, several head layouts and block sizes."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import oracle
 import synth
 from paged_kv_cache_416_amd import kernels
 
-from harness import TORCH_DTYPE, assert_close, gpu_replay, say
+from harness import TORCH_DTYPE, assert_close, gpu_replay, say, worst_margin
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +51,8 @@ def test_prefill_matches_oracle(name, mode):
             "chunk": lambda c: min(c, 1 + c // 3),
             "decode-like": lambda c: min(c, 1),
             "some-empty": lambda c: 0 if c % 2 else min(c, 37)}[mode]
-    out, ref, n = _prefill_case(w, n_of, seed=hash((name, mode)) % 1000)
+    # the query seed is a fixed function of the case id, so a failure replays with the same queries
+    out, ref, n = _prefill_case(w, n_of, seed=zlib.crc32(f"{name}/{mode}".encode()) % 1000)
     say(f"[prefill {name} {mode}] queries {n.tolist()}")
     if n.sum():
         err = assert_close(out, ref, w.dtype, f"prefill {name} {mode}")
@@ -77,12 +80,14 @@ def test_prefill_negative_scale():
 def test_prefill_peaked_softmax_and_large_values(dtype):
     """Logits spread over tens of units (scale 1, queries, keys and values N(0,1)*2): each row's
     running maximum jumps by more than the kernel's slack for its softmax reference many times, and
-    a few keys dominate. Every prompt token a query, against the oracle; one output-type ulp is
-    allowed on top of the tolerance for outputs of several units."""
+    a few keys dominate. Every prompt token a query, against the oracle. Outputs reach several units,
+    where bf16 storage alone can err by up to 2^-8 |o|, so bf16 outputs get half a bf16 ulp on top
+    of the tolerance; f16 outputs take the plain bound."""
     w = synth.decode_workload("peaked-prefill", 42, [1, 3, 40, 500, 1500], 8, 2, 128, 16, dtype, 2.0, 2.0, scale=1.0)
     out, ref, n = _prefill_case(w, lambda c: c, seed=23, q_scale=2.0)
-    err = assert_close(out, ref, w.dtype, f"prefill peaked {dtype}", storage_ulp=True)
-    say(f"  [prefill peaked {dtype}] max abs err {err:.3e}")
+    err = assert_close(out, ref, w.dtype, f"prefill peaked {dtype}", bf16_storage=dtype == "bf16")
+    say(f"  [prefill peaked {dtype}] max abs err {err:.3e}, worst |err| / (tol + tol |ref|) "
+        f"{worst_margin(out, ref, dtype):.3f}")
 
 
 def test_prefill_full_size_sampled():

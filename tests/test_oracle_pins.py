@@ -282,7 +282,8 @@ def test_lesson_note_block_table_example():
 
 
 def test_slides_table_with_unallocated_entry():
-    """Slide 10: logical blocks 0-3 map to 7, 1, 3 and nothing; the 4th entry is never read."""
+    """Slide 10: logical blocks 0-2 sit in physical blocks 7, 1 and 3, and logical block 3 has no
+    physical block yet; the 4th entry is never read."""
     g = _load("slides_block_table.json")
     B = g["block_size"]
     alloc = [b for b in g["physical_blocks"] if b is not None]

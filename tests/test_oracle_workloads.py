@@ -59,7 +59,7 @@ def test_parallel_sampling_copies_once_per_writing_branch_but_last():
     # step 1: in each prompt, k writing branches make min(k, n-1) copies of the shared partial block
     writers = (priv > 0).sum(axis=1)
     assert len(first) == int(np.minimum(writers, 3).sum())
-    # afterwards no step copies anything: only the last block is ever copied, once
+    # afterwards no step copies anything: copy-on-write duplicates a shared last block, once
     for pairs in st.step_pairs[len(st.step_pairs) - w.notes["steps"] + 1:]:
         assert pairs == []
 
