@@ -3,7 +3,9 @@
  *
  * C ABI. Plain pointers and sizes only. Host pointers are marked (host);
  * every other pointer is device memory that the CALLER allocates and owns:
- * the library never allocates, frees or retains device memory.
+ * the library never allocates or frees device memory. The one piece it holds
+ * is the static scratch array of pkv_paged_attention_decode_noalloc
+ * (PKV_NOALLOC_SCRATCH_BYTES per device, for the life of the process).
  *
  * Cache layout (both K and V): [num_blocks][num_kv_heads][block_size][head_dim],
  * row-major, head_dim innermost. Token t of a sequence lives in physical block
@@ -318,6 +320,30 @@ int pkv_paged_attention_decode_step(void *out, const void *q, const void *new_k,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                     float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
                                     int32_t dtype, uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): pkv_paged_attention_decode without the workspace
+ * arguments. A split (partition_size != 0) takes its workspace from a static device array of
+ * PKV_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it runs on until the
+ * process ends (its address is looked up once per device, on the first call there). Same kernels,
+ * same workspace layout, so results are bit-identical to pkv_paged_attention_decode with a
+ * caller-provided workspace.
+ *  All arguments: as for pkv_paged_attention_decode.
+ *  PKV_EINVAL, launching nothing, when pkv_decode_workspace_bytes(...) for this call exceeds
+ *  PKV_NOALLOC_SCRATCH_BYTES; PKV_EHIP when the array's address cannot be obtained.
+ * The call allocates nothing (no hipMalloc, no host allocation) unless PKV_DEBUG_VALIDATE=1, whose
+ * host copies it shares with the other entry points. Nothing in the array needs clearing between
+ * calls: every value a split's merge pass reads is written by the same call first. Every call on
+ * one device shares that device's array and leaves its contents behind, so calls that may overlap
+ * on one device (different streams, or several host threads) race and must be serialised by the
+ * caller, e.g. by issuing them on one stream. */
+#define PKV_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int pkv_paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                       int64_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, float scale, int32_t partition_size, int32_t dtype,
+                                       uint32_t flags, const int32_t *cached_lens, hipStream_t stream);
 
 /* Prefill (chunked) attention over the paged cache: the last n_s = query_start[s+1] -
  * query_start[s] tokens of each sequence s are queries, and query i of s, at position

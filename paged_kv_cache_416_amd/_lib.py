@@ -57,6 +57,8 @@ SIGNATURES = {
     "pkv_paged_attention_decode_step": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32,
                                                        _i32, _i32, _i32, _i32, _f32, _i32, _p, _sz, _i32, _u32, _p,
                                                        _p]),
+    "pkv_paged_attention_decode_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _i64, _p, _i32, _p, _i32, _i32, _i32, _i32,
+                                                          _i32, _i32, _f32, _i32, _i32, _u32, _p, _p]),
     "pkv_contiguous_attention_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
                                                        _f32, _i32, _p, _sz, _i32, _u32, _p]),
     "pkv_read_probe": (ctypes.c_int, [_p, _sz, _p, _p]),

@@ -35,6 +35,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "attention.h"
 
@@ -761,4 +762,76 @@ extern "C" int pkv_contiguous_attention_decode(void *out, const void *q, const v
     p.lmax = lmax;
     const int32_t grid_parts = p.partition_size > 0 ? static_cast<int32_t>(ceil_div(cap, p.partition_size)) : 1;
     return dispatch<false>(p, dtype, head_dim, kTile, num_seqs, grid_parts, flags, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation decode
+// The split workspace of pkv_paged_attention_decode_noalloc: one static array per device, held
+// until the process ends. Host code never passes `scratch` itself to a kernel (on the host that
+// name is a stand-in, not a device address): it passes the address hipGetSymbolAddress gives
+// for the current device, looked up once per device.
+static __device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device (PKV_OK), or an error.
+int scratch_address(void **out) {
+    static std::atomic<void *> cache[kMaxDevices];
+    static std::mutex setup;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PKV_EHIP, "pkv_paged_attention_decode_noalloc: no current HIP device");
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_EUNSUPPORTED, "pkv_paged_attention_decode_noalloc: device %d (at most %d devices)", dev,
+                    kMaxDevices);
+    void *p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(setup);
+        p = cache[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            const int rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                                      "pkv_paged_attention_decode_noalloc: address of the static scratch");
+            if (rc) return rc;
+            if (!p) return fail(PKV_EHIP, "pkv_paged_attention_decode_noalloc: the static scratch has no address");
+            cache[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int pkv_paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache,
+                                                  const void *v_cache, int64_t num_blocks,
+                                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                                  const int32_t *context_lens, int32_t max_context_len,
+                                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t block_size, float scale,
+                                                  int32_t partition_size, int32_t dtype, uint32_t flags,
+                                                  const int32_t *cached_lens, hipStream_t stream) {
+    const char *fn = "pkv_paged_attention_decode_noalloc";
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    if (partition_size != 0 && num_seqs > 0) {
+        // the size rule of the caller-provided workspace, checked against the static array first
+        const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size);
+        if (need > PKV_NOALLOC_SCRATCH_BYTES)
+            return fail(PKV_EINVAL, "%s: the split needs %zu bytes of workspace, the static scratch holds %zu", fn, need,
+                        static_cast<size_t>(PKV_NOALLOC_SCRATCH_BYTES));
+        if (need > 0) {
+            const int rc = scratch_address(&ws);
+            if (rc) return rc;
+            ws_bytes = PKV_NOALLOC_SCRATCH_BYTES;
+        }
+    }
+    return paged_decode(fn, out, q, k_cache, v_cache, num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                        max_context_len, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                        partition_size, ws, ws_bytes, dtype, flags, cached_lens, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, stream);
 }

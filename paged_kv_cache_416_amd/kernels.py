@@ -137,6 +137,35 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     return out
 
 
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                   partition_size=0, flags=0, cached_lens=None):
+    """paged_attention_decode with no workspace argument: a split takes its workspace from the library's
+    static per-device array (for callers that cannot allocate). Calls on one device must not overlap."""
+    _need_cuda(out, q, k_cache, v_cache, block_tables, context_lens, cached_lens)
+    S, hq, d = q.shape
+    N, hkv, B, d2 = k_cache.shape
+    if out.shape != q.shape or d2 != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    for t in (out, q, k_cache, v_cache, block_tables, context_lens):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if q.dtype != k_cache.dtype or out.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("dtype mismatch")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if cached_lens is not None and (cached_lens.dtype != torch.int32 or cached_lens.shape != (S,)
+                                    or not cached_lens.is_contiguous()):
+        raise ValueError("cached_lens must be a contiguous int32 [S]")
+    check(load().pkv_paged_attention_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), N,
+                                                    _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                                    int(max_context_len), S, hq, hkv, d, B, float(scale),
+                                                    int(partition_size), dtype_code(q.dtype), int(flags),
+                                                    _ptr(cached_lens), _stream()))
+    return out
+
+
 def paged_attention_decode_step(out, q, new_k, new_v, slot_mapping, k_cache, v_cache, block_tables, context_lens,
                                 max_context_len, scale, partition_size=0, workspace=None, flags=0, cached_lens=None):
     """reshape_and_cache(new_k, new_v, slot_mapping) then paged_attention_decode, in one launch.

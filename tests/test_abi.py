@@ -256,3 +256,16 @@ def test_prefill_wrapper_checks_the_table_shape():
     for bad in (torch.zeros(3, 2, dtype=torch.int32), torch.zeros(4, dtype=torch.int32)):
         with pytest.raises(ValueError, match="block_tables"):
             kernels.paged_attention_prefill(torch.empty_like(q), q, k, k, bad, ctx, qs, 3, 3, 0.1)
+
+
+def test_noalloc_decode_refuses_a_split_beyond_its_static_scratch():
+    """The no-allocation decode call checks the split's workspace need against its static array
+    before touching the device: 256 x 32 heads in 16-token parts of 9,216 tokens need 2.45 GB."""
+    lib = _lib.load()
+    rc = lib.pkv_paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 10, FAKE, 576, FAKE, 9216, 256, 32, 8, 128,
+                                                16, 0.1, 16, 2, 0, NULL, NULL)
+    assert rc == _lib.PKV_EINVAL
+    assert b"static scratch" in lib.pkv_last_error()
+    # the ordinary argument checks apply too
+    assert lib.pkv_paged_attention_decode_noalloc(FAKE, FAKE, FAKE, FAKE, 10, FAKE, 4, FAKE, 64, 2, 4, 4, 96, 16,
+                                                  0.1, 0, 1, 0, NULL, NULL) == _lib.PKV_EUNSUPPORTED
