@@ -44,6 +44,8 @@ namespace {
 
 constexpr int kWaves = 12;  // per-item schedule: one workgroup of three waves per SIMD on each CU
 constexpr int kThreads = kWaves * 64;
+constexpr int kWavesNarrow = 4;       // per-item schedule, short fixed partitions: three workgroups per CU
+constexpr int kSplitTilesNarrow = 32;  // partitions of at most this many tiles take the narrow workgroup
 
 template <class E, int D, int B>
 struct Shape {
@@ -319,12 +321,12 @@ __device__ inline void mha_range(const AttnParams &p, int s, int h, int t0, int 
         store_new_row<B, D * E::ELT>(p, s, kvh, c, knew, vnew);
 }
 
-// Per-item schedule: grid = (parts, num_q_heads, num_seqs), block = 64 * W; one workgroup per
+// Per-item schedule: grid = (num_q_heads, num_seqs, parts), block = 64 * W; one workgroup per
 // (sequence, query head[, partition]).
 template <class E, int D, int B, bool PAGED, int W, int POL>
 __global__ __launch_bounds__(W * 64) void attn_decode_kernel(const AttnParams p) {
     __shared__ MhaLds<W, D> lds;
-    const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int h = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
     const int64_t row_q = static_cast<int64_t>(s) * p.num_q_heads + h;
     const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
     const int t0 = p.partition_size > 0 ? part * p.partition_size : 0;
@@ -441,8 +443,21 @@ int launch(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStream_
         rc = hip_status(hipGetLastError(), "attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, D, stream);
     }
-    hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves, POL>), dim3(grid_parts, p.num_q_heads, num_seqs),
-                       dim3(kThreads), 0, stream, p);
+    if (grid_parts > 65535)
+        return fail(PKV_EINVAL, "attention: %d partitions per sequence exceed the grid (65535)", grid_parts);
+    // Grid (heads, sequences, partitions): workgroups are dealt to the XCDs round-robin in this
+    // order, so each XCD serves every eighth head across all sequences and partitions, an even
+    // share. (Partitions fastest would give each XCD a fixed partition index, and the later
+    // partitions exist only for the longer sequences.) A fixed partition of at most 32 tiles goes
+    // to 4 waves, so each still walks up to 8 tiles through its register pipeline; longer ranges
+    // (one pass, larger partitions) to 12.
+    constexpr int TR = Shape<E, D, B>::TR;
+    const dim3 grid(p.num_q_heads, num_seqs, grid_parts);
+    if (p.partition_size > 0 && p.partition_size <= kSplitTilesNarrow * TR)
+        hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWavesNarrow, POL>), grid, dim3(kWavesNarrow * 64), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((attn_decode_kernel<E, D, B, PAGED, kWaves, POL>), grid, dim3(kThreads), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "attention launch");
     if (rc || p.partition_size <= 0) return rc;
     return launch_reduce(p, E::CODE, D, num_seqs, stream);

@@ -27,6 +27,7 @@ import numpy as np
 _LENGTHS, _FREE, _Q, _KV, _PREFIX, _PROMPT = 1, 2, 3, 4, 5, 6
 _SYSTEM, _SYSKV, _TOKENS = 7, 8, 9
 _REQUESTS = 10
+_SCORES = 11
 
 DTYPES = ("f32", "f16", "bf16")
 ELT_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -310,6 +311,38 @@ def parallel_sampling(seed=3, prompts=8, n=4, prompt_len=512, max_extra=15, max_
                     scale=float(np.float32(1.0 / math.sqrt(d))), partition_size=0, ops=ops,
                     batch=list(range(S)), q=q, lmax=int((L0[:, None] + pb).max()), value_scale=0.5,
                     notes={"s_p": sp.tolist(), "private": pb.tolist(), "steps": steps, "checks": checks})
+
+
+def beam_search(seed=8, beams=4, fanout=3, steps=12, prompt_len=70, hq=8, hkv=8, d=128, block_size=16,
+                dtype="f16"):
+    """A beam-search schedule over one prompt, as seeded draws only: the prompt's K/V rows, and per
+    step one score per candidate (each of the ``beams`` live beams forks ``fanout`` candidates, and the
+    ``beams`` highest scores survive), the surviving beams' new K/V rows and their queries.
+
+    The scores stand in for a model's sequence log-probabilities; which candidate survives is
+    scheduling, not the method's arithmetic. A prompt whose length is not a multiple of the block
+    size leaves a partly filled last block that every beam shares, so the first step copies it.
+    """
+    r = _rng(seed, _SCORES)
+    pk = _draw_kv(seed, _PROMPT, [()], [prompt_len], hkv, d, 0.5, dtype)[0]
+    sched = []
+    live = 1  # the prompt's sequence
+    for t in range(steps):
+        keep = min(beams, live * fanout)
+        kr = _rng(seed, _KV, t)
+        sched.append({
+            "scores": r.random(live * fanout),
+            "k": normal(kr, (keep, hkv, d), 0.5, dtype),
+            "v": normal(kr, (keep, hkv, d), 0.5, dtype),
+            "q": normal(_rng(seed, _Q, t), (keep, hq, d), 0.5, dtype),
+        })
+        live = keep
+    # blocks: the prompt's, plus at most one new block per surviving beam per step
+    nb = _pool_size(-(-prompt_len // block_size) + beams * (steps + 1))
+    free_order = _rng(seed, _FREE).permutation(nb).astype(np.int32)
+    return {"prompt_k": pk[0], "prompt_v": pk[1], "steps": sched, "beams": beams, "fanout": fanout,
+            "num_blocks": nb, "free_order": free_order, "block_size": block_size, "dtype": dtype,
+            "hq": hq, "hkv": hkv, "d": d, "scale": float(np.float32(1.0 / math.sqrt(d)))}
 
 
 def prefix_cache_requests(seed=6, system_lens=(69, 128, 200), requests=12, private=(1, 100), hq=16, hkv=8,
