@@ -35,15 +35,15 @@ PARTITION_BALANCED = -1  # the library's balanced split mode
 FLAG_CACHED_KV = 2  # the library's cached K/V load flag
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = "paged_kv_cache_416_amd/csrc/"
-# workload -> (counter summary under profiles/, sources of its attention kernel, kernel name part,
-#              partition size, flags and cached-load hint the summary was taken at)
+# counter summaries under profiles/: name -> (workload, sources of its attention kernel, kernel name
+# part, partition size, flags and cached-load hint the summary was taken at)
+_GQA_SOURCES = [CSRC + "attention_gqa.hip", CSRC + "mfma.h", CSRC + "attention.h", CSRC + "common.h"]
 COUNTERS = {
-    "13b-decode": ("attn_decode_f16_13b_counters.txt",
-                   [CSRC + "attention.hip", CSRC + "attention.h", CSRC + "common.h"],
-                   "attn_decode_kernel", 0, 0, "none"),
-    "8b-gqa-prefix": ("attn_gqa_bf16_8b_balanced_counters.txt",
-                      [CSRC + "attention_gqa.hip", CSRC + "mfma.h", CSRC + "attention.h", CSRC + "common.h"],
-                      "attn_gqa_balanced_kernel", PARTITION_BALANCED, 0, "shared"),
+    "attn_decode_f16_13b_counters.txt": ("13b-decode", [CSRC + "attention.hip", CSRC + "attention.h", CSRC + "common.h"],
+                                         "attn_decode_kernel", 0, 0, "none"),
+    "attn_gqa_bf16_8b_balanced_counters.txt": ("8b-gqa-prefix", _GQA_SOURCES, "attn_gqa_balanced_kernel",
+                                               PARTITION_BALANCED, 0, "shared"),
+    "attn_gqa_bf16_8b_p512_counters.txt": ("8b-gqa-prefix", _GQA_SOURCES, "attn_gqa_mfma_kernel", 512, 0, "shared"),
 }
 
 
@@ -90,6 +90,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--no-gqa-leg", action="store_true",
+                    help="with the 13B workload, skip the 8B-shaped grouped-query leg (gqa_8b)")
     ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
     ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
     ap.add_argument("--prefill", type=int, default=0, metavar="PROMPT_LEN",
@@ -108,6 +110,9 @@ def parse():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT", "CMD"))
     ap.add_argument("--summarize-counters", nargs=6,
                     metavar=("WORKLOAD_NAME", "FETCH_CSV", "WRITE_CSV", "OUT", "CMD1", "CMD2"))
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="OUT KERNEL_PART TITLE CSV CMD [CSV CMD ...]: per-dispatch means of every counter of "
+                         "rocprofv3 --pmc passes for the kernels whose name contains KERNEL_PART")
     return ap.parse_args()
 
 
@@ -169,102 +174,100 @@ def timed_launches(fn, n, stream):
 
 
 def read_counters(workload, P, flags, hint):
-    """Measured HBM bytes per attention launch from the committed counter summary, if it was
-    taken at this partition size, flags and cached-load hint on the kernel source as it is now;
-    else None."""
-    entry = COUNTERS.get(workload)
-    if entry is None or (P, flags, hint) != (entry[3], entry[4], entry[5]):
-        return None
-    path = os.path.join(PROFILES, entry[0])
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as fh:
-        for line in fh:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != source_hash(entry[1]):
-        return None
-    return float(kv["traffic_bytes_per_dispatch"])
+    """Measured HBM bytes per attention launch from the committed counter summary taken on this
+    workload at this partition size, flags and cached-load hint, on the kernel source as it is
+    now; else None."""
+    for fname, entry in COUNTERS.items():
+        if entry[0] != workload or (P, flags, hint) != (entry[3], entry[4], entry[5]):
+            continue
+        path = os.path.join(PROFILES, fname)
+        if not os.path.exists(path):
+            return None
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != source_hash(entry[1]):
+            return None
+        return float(kv["traffic_bytes_per_dispatch"])
+    return None
 
 
-def main():
-    args = parse()
-    if args.summarize_trace:
-        return summarize_trace(*args.summarize_trace)
-    if args.summarize_counters:
-        return summarize_counters(*args.summarize_counters)
-    if args.cpu_one_thread:
-        return cpu_one_thread(args.cpu_one_thread[0], int(args.cpu_one_thread[1]))
-    if args.memory_sim:
-        print(json.dumps(memory_sim_leg()))
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The path shards by sequence or by "
-              f"KV head with no exchange between GPUs, so one GPU's figure at its share of the batch is the "
-              f"per-GPU figure.", file=sys.stderr)
-        sys.exit(2)
+class Setup:
+    """One workload's device state for timing: the cache built by every op but the decode step's own
+    append, `replicas` copies of the caches, the step's new rows and slots, tables and queries."""
 
-    import numpy as np
+    def __init__(self, w, args, dev, hint):
+        import numpy as np
+        import torch
+
+        from paged_kv_cache_416_amd.cache import PagedKVCache, run_ops, to_device
+
+        self.w, self.dev = w, dev
+        self.dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        dt, B = self.dt, w.block_size
+        cache = PagedKVCache(w.num_blocks, B, w.num_kv_heads, w.head_dim, dt, device=dev, free_order=w.free_order)
+        run_ops(cache, w.ops[:-1], dt)
+        step = w.ops[-1][1]  # [(sid, k[1,Hkv,D], v[1,Hkv,D]), ...]
+        slots, pairs = cache.pool.append([(sid, k.shape[0]) for sid, k, _ in step])
+        assert len(pairs) == 0
+        # a step's new rows in batch order (one token per sequence), for the one-launch step
+        assert [sid for sid, _, _ in step] == list(w.batch)
+        self.cache = cache
+        self.n_new = len(step)
+        self.new_k = to_device(np.concatenate([k for _, k, _ in step]), dt, dev)
+        self.new_v = to_device(np.concatenate([v for _, _, v in step]), dt, dev)
+        self.slot_dev = torch.from_numpy(slots).to(dev)
+        self.tb_host, self.ctx_host = cache.pool.tables(w.batch)
+        self.tb = torch.from_numpy(self.tb_host).to(dev)
+        self.ctx_dev = torch.from_numpy(self.ctx_host).to(dev)
+        self.max_ctx = int(self.ctx_host.max())
+        self.hint = hint
+        self.cached_lens = cache.shared_prefix_lens(w.batch) if hint == "shared" else None
+        self.ctx = w.final_lengths()
+        self.q = to_device(w.q, dt, dev)
+        self.out = torch.empty_like(self.q)
+        self.replicas = args.replicas
+        self.ks = [cache.k] + [cache.k.clone() for _ in range(args.replicas - 1)]
+        self.vs = [cache.v] + [cache.v.clone() for _ in range(args.replicas - 1)]
+        torch.cuda.synchronize()
+        elt = w.elt_bytes
+        self.logical_b, self.unique_b = attention_bytes(self.ctx, w.num_q_heads, w.num_kv_heads, w.head_dim, elt, B,
+                                                        unique_rows(self.tb_host, self.ctx_host, B))
+        # K1: read + write K and V of each new token, and its slot
+        self.w_bytes = 2 * 2 * self.n_new * w.num_kv_heads * w.head_dim * elt + 8 * self.n_new
+
+
+def measure(st, P, flags, args, step_mode, percentiles=True):
+    """Time one workload in one split mode: whole decode steps (host clock, `steps` steps after
+    `warmup`), the other step form, and the attention launches alone (HIP events on the launch
+    stream) for the roofline."""
     import torch
 
     from paged_kv_cache_416_amd import kernels
-    from paged_kv_cache_416_amd.cache import PagedKVCache, run_ops, to_device
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w, default_P, default_flags = make_workload(args.workload)
-    flags = default_flags if args.flags < 0 else args.flags
-    hint = args.cached_lens if args.cached_lens != "default" else ("shared" if args.workload == "gqa" else "none")
-    step_mode = args.step
-    P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
-    if P is None:
-        P = int(args.partition)
-    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-    S, hq, hkv, d, B, elt = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.elt_bytes
-
-    # build the cache state: every op but the decode step's own append
-    cache = PagedKVCache(w.num_blocks, B, hkv, d, dt, device=dev, free_order=w.free_order)
-    run_ops(cache, w.ops[:-1], dt)
-    step = w.ops[-1][1]  # [(sid, k[1,Hkv,D], v[1,Hkv,D]), ...]
-    slots, pairs = cache.pool.append([(sid, k.shape[0]) for sid, k, _ in step])
-    assert len(pairs) == 0
-    new_k = to_device(np.concatenate([k for _, k, _ in step]), dt, dev)
-    new_v = to_device(np.concatenate([v for _, _, v in step]), dt, dev)
-    slot_dev = torch.from_numpy(slots).to(dev)
-    tb_host, ctx_host = cache.pool.tables(w.batch)
-    tb = torch.from_numpy(tb_host).to(dev)
-    ctx_dev = torch.from_numpy(ctx_host).to(dev)
-    max_ctx = int(ctx_host.max())
-    cached_lens = cache.shared_prefix_lens(w.batch) if hint == "shared" else None
-    ctx = w.final_lengths()
-    q = to_device(w.q, dt, dev)
-    out = torch.empty_like(q)
-    ws = kernels.alloc_workspace(S, hq, d, max_ctx, P, dev)
-    ks = [cache.k] + [cache.k.clone() for _ in range(args.replicas - 1)]
-    vs = [cache.v] + [cache.v.clone() for _ in range(args.replicas - 1)]
-    torch.cuda.synchronize()
-
-    logical_b, unique_b = attention_bytes(ctx, hq, hkv, d, elt, B, unique_rows(tb_host, ctx_host, B))
-    w_bytes = 2 * 2 * len(step) * hkv * d * elt + 8 * len(step)  # K1: read + write K and V, slots
+    w = st.w
+    S, hq, d = w.num_seqs, w.num_q_heads, w.head_dim
+    ws = kernels.alloc_workspace(S, hq, d, st.max_ctx, P, st.dev)
     stream = torch.cuda.current_stream()
+    R = st.replicas
 
     def attend(i):
-        r = i % args.replicas
-        kernels.paged_attention_decode(out, q, ks[r], vs[r], tb, ctx_dev, max_ctx, w.scale, P, ws, flags, cached_lens)
+        r = i % R
+        kernels.paged_attention_decode(st.out, st.q, st.ks[r], st.vs[r], st.tb, st.ctx_dev, st.max_ctx, w.scale, P, ws,
+                                       flags, st.cached_lens)
 
-    # a step's new rows in batch order (one token per sequence), for the one-launch step
-    assert [sid for sid, _, _ in step] == list(w.batch) and new_k.shape[0] == S
     def separate_step(i):
-        r = i % args.replicas
-        kernels.reshape_and_cache(new_k, new_v, ks[r], vs[r], slot_dev)
+        r = i % R
+        kernels.reshape_and_cache(st.new_k, st.new_v, st.ks[r], st.vs[r], st.slot_dev)
         attend(i)
 
     def fused_step(i):
-        r = i % args.replicas
-        kernels.paged_attention_decode_step(out, q, new_k, new_v, slot_dev, ks[r], vs[r], tb, ctx_dev, max_ctx,
-                                            w.scale, P, ws, flags, cached_lens)
+        r = i % R
+        kernels.paged_attention_decode_step(st.out, st.q, st.new_k, st.new_v, st.slot_dev, st.ks[r], st.vs[r], st.tb,
+                                            st.ctx_dev, st.max_ctx, w.scale, P, ws, flags, st.cached_lens)
 
     def time_steps(fn, steps):
         for i in range(args.warmup):
@@ -287,11 +290,60 @@ def main():
     ms_other = time_steps(other_step, args.steps)
     # the attention launches alone, for the roofline
     attn_us = timed_launches(attend, args.steps, stream)
-    attn_pct = launch_percentiles(attend, max(100, args.steps), stream)
+    value = (st.unique_b + st.w_bytes) / (ms_per_step * 1e-3) / 1e9
+    achieved = st.unique_b / (attn_us * 1e-6) / 1e9
+    traffic = read_counters(w.name, P, flags, st.hint)
+    res = {
+        "ms_per_step": ms_per_step,
+        "ms_other": ms_other,
+        "value": value,
+        "attention_us": attn_us,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": round(traffic) if traffic is not None else None,
+                     "kernel": kernel_label(w, P, flags)},
+    }
+    if percentiles:
+        res["attention_us_single_launch"] = launch_percentiles(attend, max(100, args.steps), stream)
+    return res
 
-    value = (unique_b + w_bytes) / (ms_per_step * 1e-3) / 1e9
-    achieved = unique_b / (attn_us * 1e-6) / 1e9
-    traffic = read_counters(w.name, P, flags, hint)
+
+def main():
+    args = parse()
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters)
+    if args.summarize_pmc:
+        a = args.summarize_pmc
+        return summarize_pmc(a[0], a[1], a[2], list(zip(a[3::2], a[4::2])))
+    if args.cpu_one_thread:
+        return cpu_one_thread(args.cpu_one_thread[0], int(args.cpu_one_thread[1]))
+    if args.memory_sim:
+        print(json.dumps(memory_sim_leg()))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported. The path shards by sequence or by "
+              f"KV head with no exchange between GPUs, so one GPU's figure at its share of the batch is the "
+              f"per-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w, default_P, default_flags = make_workload(args.workload)
+    flags = default_flags if args.flags < 0 else args.flags
+    hint = args.cached_lens if args.cached_lens != "default" else ("shared" if args.workload == "gqa" else "none")
+    step_mode = args.step
+    P = {"default": default_P, "balanced": PARTITION_BALANCED}.get(args.partition)
+    if P is None:
+        P = int(args.partition)
+    st = Setup(w, args, dev, hint)
+    S, hq, hkv, d, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    m = measure(st, P, flags, args, step_mode)
+    ms_per_step, attn_us, value = m["ms_per_step"], m["attention_us"], m["value"]
+    ctx = st.ctx
 
     result = {
         "metric": METRIC,
@@ -315,15 +367,16 @@ def main():
         "decode_tokens_per_s_attention_only": {
             "layers": LAYERS.get(w.name, 40),
             "value": round(S / (LAYERS.get(w.name, 40) * attn_us * 1e-6), 1)},
-        "ms_per_step_" + ("separate" if step_mode == "fused" else "fused"): round(ms_other, 5),
+        "ms_per_step_" + ("separate" if step_mode == "fused" else "fused"): round(m["ms_other"], 5),
         "attention_us": round(attn_us, 2),
-        "attention_us_single_launch": attn_pct,
-        "bytes_per_step": {"attention_logical": logical_b, "attention_unique": unique_b, "cache_write": w_bytes},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": round(traffic) if traffic is not None else None,
-                     "kernel": kernel_label(w, P, flags)},
+        "attention_us_single_launch": m["attention_us_single_launch"],
+        "bytes_per_step": {"attention_logical": st.logical_b, "attention_unique": st.unique_b,
+                           "cache_write": st.w_bytes},
+        "roofline": m["roofline"],
     }
+    unique_b = st.unique_b
+    cache = st.cache
+    dt = st.dt
 
     if args.copy_probe:
         # a plain elementwise kernel that reads and writes a known number of bytes, by which the
@@ -354,7 +407,40 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.workload, P, unique_b, args.cpu_seconds)
 
+    if args.workload == "13b" and not args.no_gqa_leg:
+        del st, cache
+        torch.cuda.empty_cache()
+        result["gqa_8b"] = gqa_leg(args, dev, with_cpu=not args.no_cpu_baseline)
+
     print(json.dumps(result), flush=True)
+
+
+def gqa_leg(args, dev, with_cpu=True):
+    """The 8B-shaped grouped-query workload (32 query / 8 KV heads, bf16, 256 sequences over a shared
+    1024-token prefix): whole decode steps and the attention launches at its configured split
+    (partitions of 512 tokens, then the merge pass) and in the balanced mode, each with its own
+    roofline on unique bytes (each physical block once); the oracle on the same batch beside it."""
+    w, P_cfg, flags = make_workload("gqa")
+    st = Setup(w, args, dev, "shared")
+    res = {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+           "head_dim": w.head_dim, "block_size": w.block_size, "dtype": w.dtype, "sum_context": int(st.ctx.sum()),
+           "max_context": int(st.ctx.max()), "cached_lens": "shared",
+           "bytes_per_step": {"attention_logical": st.logical_b, "attention_unique": st.unique_b,
+                              "cache_write": st.w_bytes}}
+    for label, P in (("configured_split", P_cfg), ("balanced", PARTITION_BALANCED)):
+        m = measure(st, P, flags, args, "fused", percentiles=False)
+        res[label] = {"partition_size": P, "ms_per_step": round(m["ms_per_step"], 5),
+                      "value": round(m["value"], 2), "unit": "GB/s",
+                      "pct_hbm_peak": round(100 * m["value"] / PEAK_HBM_GBS, 2),
+                      "attention_us": round(m["attention_us"], 2),
+                      "decode_tokens_per_s": round(w.num_seqs / (m["ms_per_step"] * 1e-3), 1),
+                      "decode_tokens_per_s_attention_only": {
+                          "layers": LAYERS[w.name],
+                          "value": round(w.num_seqs / (LAYERS[w.name] * m["attention_us"] * 1e-6), 1)},
+                      "roofline": m["roofline"]}
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, "gqa", P_cfg, st.unique_b, args.cpu_seconds / 2, one_thread=False)
+    return res
 
 
 def swap_leg(cache, w, dev, dt, reps=5):
@@ -592,9 +678,9 @@ def contiguous_leg(w, P, args, dev, dt, paged_us, flags):
     return {"attention_us": round(us, 2), "paged_over_contiguous": round(paged_us / us - 1.0, 4)}
 
 
-def cpu_baseline(w, workload, P, a_bytes, seconds):
+def cpu_baseline(w, workload, P, a_bytes, seconds, one_thread=True):
     """The oracle (plain fp64 C, OpenMP over (sequence, head)) on the host cores, same workload;
-    and one call of it on one thread, in a child process started with OMP_NUM_THREADS=1."""
+    and (one_thread) one call of it on one thread, in a child process started with OMP_NUM_THREADS=1."""
     import subprocess
 
     import oracle
@@ -611,6 +697,8 @@ def cpu_baseline(w, workload, P, a_bytes, seconds):
            "kind": "oracle", "sample": f"the full {w.name} batch ({w.num_seqs} sequences), {reps} calls in "
                                        f"{t:.1f} s, {per_call * 1e3:.1f} ms per call",
            "decode_tokens_per_s": round(w.num_seqs / per_call, 2), "cpu_model": cpu_model()}
+    if not one_thread:
+        return res
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-one-thread", workload, str(P)], env=env,
                        capture_output=True, text=True, timeout=300)
@@ -676,7 +764,7 @@ def summarize_counters(workload, fetch_csv, write_csv, out, cmd_fetch, cmd_write
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     probe = [k for k in fetch if "neg_kernel" in k]
-    _, sources, kname, _, _, _ = COUNTERS[workload]
+    _, sources, kname, _, _, _ = COUNTERS[os.path.basename(out)]
     attn = [k for k in fetch if kname in k]
     if len(probe) != 1 or len(attn) != 1:
         raise SystemExit(f"expected one probe and one attention kernel, got {probe} / {attn}")
@@ -701,6 +789,28 @@ def summarize_counters(workload, fetch_csv, write_csv, out, cmd_fetch, cmd_write
              f"fetch_scale: {fs:.4f}",
              f"write_scale: {wsc:.4f}",
              f"traffic_bytes_per_dispatch: {traffic:.0f}"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(out, kernel_part, title, passes):
+    """rocprofv3 --pmc passes (one counter set each) -> the mean value per dispatch of every counter,
+    for each kernel whose name contains kernel_part, with the command of each pass."""
+    per = {}  # kernel -> counter -> [values]
+    for path, _ in passes:
+        for r in csv.DictReader(open(path)):
+            if kernel_part not in r["Kernel_Name"]:
+                continue
+            per.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    lines = [f"# {title}", "# rocprofv3 --pmc, one pass per counter set; values are means per dispatch"]
+    for path, cmd in passes:
+        lines.append(f"# command: {cmd}")
+    for k, cs in per.items():
+        lines.append(f"kernel: {k}")
+        for c, v in cs.items():
+            lines.append(f"  {c}: {sum(v) / len(v):.6g}  (dispatches {len(v)})")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int s = blockIdx.z, kvh = blockIdx.y;
+    const int kvh = blockIdx.x, s = blockIdx.y;
     const int G = p.group;
     // per-sequence values, uniform (scalar registers): the buffer resources built from them
     // stay scalar, with no per-lane loop around the loads
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int nq = __builtin_amdgcn_readfirstlane(p.query_start[s + 1]) - q0;
     const int ctx = clamp_ctx(__builtin_amdgcn_readfirstlane(p.ctx_lens[s]), p.ctx_cap);
     const int rows = nq * G;
-    const int wg_row0 = (gridDim.x - 1 - blockIdx.x) * W * RT * 16;
+    const int wg_row0 = (gridDim.z - 1 - blockIdx.z) * W * RT * 16;
     // uniform over the workgroup; a sequence whose rows are not all inside q and out is skipped
     if (nq <= 0 || nq > ctx || q0 < 0 || q0 > p.num_tokens - nq || wg_row0 >= rows) return;
     const int row0 = wg_row0 + wave * RT * 16;  // a wave past the last row still loads and waits
@@ -313,10 +313,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 template <class E, int B>
 int launch(const PrefillParams &p, int32_t max_query_len, int32_t num_seqs, hipStream_t stream) {
     const int64_t tiles = ceil_div(static_cast<int64_t>(max_query_len) * p.group, 16);
-    const int64_t gx = ceil_div(tiles, kPrefillWaves * kPrefillRowTiles);
-    if (gx > INT32_MAX) return fail(PKV_EINVAL, "pkv_paged_attention_prefill: max_query_len too large");
+    const int64_t gz = ceil_div(tiles, kPrefillWaves * kPrefillRowTiles);
+    if (gz > 65535) return fail(PKV_EINVAL, "pkv_paged_attention_prefill: max_query_len too large");
+    // Grid (kv heads, sequences, row blocks), the row blocks last and in reverse: workgroups are
+    // dispatched in linear order, so every (kv head, sequence) pair's last rows, which need the
+    // most keys, go first, and the light first rows of all pairs fill in at the end (longest
+    // first). The kv head fastest deals each kv head to one XCD, whose L2 then holds its keys.
     hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles>),
-                       dim3(static_cast<unsigned>(gx), p.num_kv_heads, num_seqs), dim3(kPrefillWaves * 64), 0, stream,
+                       dim3(p.num_kv_heads, num_seqs, static_cast<unsigned>(gz)), dim3(kPrefillWaves * 64), 0, stream,
                        p);
     return hip_status(hipGetLastError(), "pkv_paged_attention_prefill launch");
 }
