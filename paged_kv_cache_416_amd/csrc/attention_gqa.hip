@@ -319,6 +319,39 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, t0, t1, sink, lds);
 }
 
+// The fixed-partition merge of one (sequence, kv head): grid = (num_kv_heads, num_seqs), the kv
+// head fastest like the attention grid, so a workgroup reads the partials its XCD's L2 received;
+// 256 threads over the group's G heads x 128 columns. One pass over the partitions with a
+// running maximum (the partitions' loads are independent):
+//   M = max_p m_p, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
+template <class E>
+__global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const AttnParams p) {
+    constexpr int D = 128;
+    const int kvh = blockIdx.x, s = blockIdx.y, G = p.group;
+    const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
+    const int np = (ctx + p.partition_size - 1) / p.partition_size;
+    const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+        const int j = i / D, d = i % D;
+        const int64_t wr = (row_q0 + j) * p.num_parts;
+        const float *wacc = p.ws + wr * D + d;
+        const float *wm = p.ws + p.ws_rows * D + wr;
+        const float *wl = p.ws + p.ws_rows * (D + 1) + wr;
+        float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 4
+        for (int k = 0; k < np; ++k) {
+            const float mg = wm[k], lg = wl[k], og = wacc[static_cast<int64_t>(k) * D];
+            const float Mn = fmaxf(M, mg);
+            const float Mr = Mn == -INFINITY ? 0.f : Mn;
+            const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
+            L = fmaf(lg, f, L * a);
+            O = fmaf(og, f, O * a);
+            M = Mn;
+        }
+        E::store(p.out, (row_q0 + j) * D + d, L > 0.f ? O / L : 0.f);
+    }
+}
+
 // Balanced schedule: grid = balanced_wgs workgroups (one per CU), each an equal share of the
 // batch's tiles (work rows = (kv head, sequence), head-major); cut rows are merged by the
 // balanced reduce pass. One workgroup per CU because two sharing a CU do not progress at one
@@ -356,7 +389,8 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
                        dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
     if (rc || p.partition_size <= 0) return rc;
-    return launch_reduce(p, E::CODE, 128, num_seqs, stream);
+    hipLaunchKernelGGL((attn_gqa_reduce_kernel<E>), dim3(p.num_kv_heads, num_seqs), dim3(256), 0, stream, p);
+    return hip_status(hipGetLastError(), "grouped-query reduce launch");
 }
 
 template <class E, int B>

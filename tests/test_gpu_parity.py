@@ -351,6 +351,39 @@ def test_balanced_at_the_sequence_limit(dtype, hq, hkv, d):
     assert e.value.code == PKV_EUNSUPPORTED
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,lengths,parts", [
+    # 4096 sequences of 0-40 tokens: partitions of one or two tiles, empty sequences
+    ("bf16", 16, 4, ("uniform", 4096, 0, 40), (16, 32)),
+    # a few long contexts among short ones: many partitions per row, a ragged last one
+    ("f16", 64, 8, ("mixed", 300, 1, 9000), (16, 512, 2048)),
+    # groups of 8 and 16 heads (the merge pass covers a group's heads with 256 threads)
+    ("bf16", 8, 1, ("uniform", 40, 1, 3000), (256,)),
+    ("bf16", 16, 1, ("uniform", 40, 1, 3000), (256,)),
+])
+def test_fixed_partitions_ragged_and_many(dtype, hq, hkv, lengths, parts):
+    """Fixed partitions on the matrix-core path (each partition computed on its own, then the merge
+    pass over a (sequence, kv head) group's partitions): thousands of one- and two-tile partitions
+    with empty sequences among them, a few long contexts among short ones, and groups up to 16
+    heads, against the oracle; a second call is bit-identical."""
+    kind, n, lo, hi = lengths
+    r = np.random.default_rng(77)
+    if kind == "uniform":
+        lens = r.integers(lo, hi + 1, size=n)
+    else:
+        lens = r.integers(lo, 200, size=n)
+        lens[r.choice(n, 6, replace=False)] = hi
+    w = synth.decode_workload("parts", 38, lens, hq, hkv, 128, 16, dtype, 0.5, 0.5)
+    say(f"[parts {dtype} Hq={hq} Hkv={hkv}] S={w.num_seqs} max ctx {int(lens.max())} blocks={w.num_blocks}")
+    st = oracle.replay(w)
+    ref = oracle.attention_of(st, w)
+    c = gpu_replay(w)
+    for P in parts:
+        out = gpu_attention(c, w, partition_size=P)
+        err = assert_close(out, ref, dtype, f"parts P={P}")
+        assert bits_equal(gpu_attention(c, w, partition_size=P), out), "a second call differs"
+        say(f"  P={P} max abs err {err:.3e}")
+
+
 @pytest.mark.parametrize("one_launch", [False, True])
 @pytest.mark.parametrize("P", [0, BALANCED])
 def test_decode_step_in_a_hip_graph(P, one_launch):
