@@ -85,6 +85,16 @@ __device__ inline unsigned word(const u32x4 &r, int w) {
     return w == 0 ? r.x : (w == 1 ? r.y : (w == 2 ? r.z : r.w));
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16): every lane addresses 8 bytes (four 16-bit values);
+// within each group of 16 lanes, lane r receives as its element j the element r % 4 of the four
+// that lane 4j + r / 4 of the group addressed. With lane (n, g) of a group addressing row
+// r0 + 4g + n / 4, columns c0 + 4 (n % 4) .. + 3 of a row-major 16-bit tile, lane (n, g) receives
+// column c0 + n of rows r0 + 4g .. r0 + 4g + 3: a column of the tile, as an MFMA operand wants it.
+__device__ inline u32x2 lds_read_tr16(const void *p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
 // Table entries as scalar loads: the constant address space (the tables are not written while
 // a kernel runs) with a uniform index gives s_load, whose completion counter is not the one the
 // K/V loads use, so looking an entry up never waits for K/V data.

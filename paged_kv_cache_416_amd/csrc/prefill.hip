@@ -170,12 +170,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int kk = 0; kk < 4; ++kk) c[rt][u] = M::mma(kf[kk], qv[rt][kk], c[rt][u]);
             }
         }
-        u32x4 vf[2][4];  // rows u * 16 + 4g + i, 16-byte column n
+        // V^T operand of weighted-sum MFMA j (d = 16 j + n): k slots 8g .. 8g+3 are keys 4g .. 4g+3
+        // of the first 16-key tile and 8g+4 .. 8g+7 the same keys of the second, one transposed
+        // LDS read each (lane (n, g) addresses row 4g + n / 4, columns 16 j + 4 (n % 4) .. + 3)
+        u32x4 vt[8];
+        {
+            const char *vb = &lds[b][1][4 * g + (n >> 2)][(n & 3) * 8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vf[u][i] = *reinterpret_cast<const u32x4 *>(&lds[b][1][u * TR + 4 * g + i][n * 16]);
+            for (int j = 0; j < 8; ++j) {
+                const u32x2 a = lds_read_tr16(vb + j * 32), c2 = lds_read_tr16(vb + TR * kLdsRow + j * 32);
+                vt[j] = u32x4{a.x, a.y, c2.x, c2.y};
+            }
+        }
         // The row tiles' softmax runs phase by phase over all of them, with one branch per phase
         // at most, so the tiles' independent chains share basic blocks and interleave.
         float sc[RT][2][4], mloc[RT];
@@ -245,15 +251,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 }
             const u32x4 ph = {h[0], h[1], h[2], h[3]}, pr = {r[0], r[1], r[2], r[3]};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = j >> 1;
-                const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                const u32x4 vt = {__builtin_amdgcn_perm(word(vf[0][1], w), word(vf[0][0], w), sel),
-                                  __builtin_amdgcn_perm(word(vf[0][3], w), word(vf[0][2], w), sel),
-                                  __builtin_amdgcn_perm(word(vf[1][1], w), word(vf[1][0], w), sel),
-                                  __builtin_amdgcn_perm(word(vf[1][3], w), word(vf[1][2], w), sel)};
-                acc[rt][j] = M::mma(vt, pr, M::mma(vt, ph, acc[rt][j]));
-            }
+            for (int j = 0; j < 8; ++j) acc[rt][j] = M::mma(vt[j], pr, M::mma(vt[j], ph, acc[rt][j]));
             // the weight sums on the matrix cores: an all-ones operand in place of V^T gives
             // every row of the product the column sum of P^T, the same fp32 accumulation
             lsum[rt] = M::mma(kOnes, pr, M::mma(kOnes, ph, lsum[rt]));
@@ -295,7 +293,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         step(R[1], 1);
     }
 
-    // lane (n, g) holds row n's weight sum and d = 8 (4g + i) + j of its output
+    // lane (n, g) holds row n's weight sum and d = 16 j + 4g + i of its output
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float l = lsum[rt][0];
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) E::store(p.out, base + 8 * (4 * g + i) + j, acc[rt][j][i] * inv);
+                for (int j = 0; j < 8; ++j) E::store(p.out, base + 16 * j + 4 * g + i, acc[rt][j][i] * inv);
         }
     }
 }
