@@ -142,7 +142,9 @@ def kernel_label(w, P, flags):
             and g <= 16 and not flags & 1)
     if P == PARTITION_BALANCED:
         return ("attn_gqa_balanced_kernel" if mfma else "attn_decode_balanced_kernel") + "+attn_reduce_balanced_kernel"
-    return ("attn_gqa_mfma_kernel" if mfma else "attn_decode_kernel") + ("+attn_reduce_kernel" if P > 0 else "")
+    if mfma:
+        return "attn_gqa_mfma_kernel" + ("+attn_gqa_reduce_kernel" if P > 0 else "")
+    return "attn_decode_kernel" + ("+attn_reduce_kernel" if P > 0 else "")
 
 
 def launch_percentiles(fn, n, stream):
@@ -603,10 +605,16 @@ def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=30, war
     def run(i):
         kernels.paged_attention_prefill(out, q, k, v, tables, ctx, qs, prompt_len, prompt_len, d ** -0.5)
 
-    # a long warm-up: after the decode legs' host-side work the first tens of launches run up to
-    # 8 % slow while the device returns to its steady clocks
-    for i in range(warmup):
+    # a long warm-up, at least `warmup` launches and half a second of them: after the other legs'
+    # host-side work (the prefix cache, the oracle) the device comes back at lower clocks, and the
+    # first tens of milliseconds of launches run several per cent slow
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < 0.5:
         run(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     us = timed_launches(run, reps, stream)
     flops = 4 * d * hq * seqs * prompt_len * (prompt_len + 1) / 2
     tf = flops / (us * 1e-6) / 1e12
