@@ -43,7 +43,7 @@ COUNTERS = {
                                          "attn_decode_kernel", 0, 0, "none"),
     "attn_gqa_bf16_8b_balanced_counters.txt": ("8b-gqa-prefix", _GQA_SOURCES, "attn_gqa_balanced_kernel",
                                                PARTITION_BALANCED, 0, "shared"),
-    "attn_gqa_bf16_8b_p512_counters.txt": ("8b-gqa-prefix", _GQA_SOURCES, "attn_gqa_mfma_kernel", 512, 0, "shared"),
+    "attn_gqa_bf16_8b_p512_counters.txt": ("8b-gqa-prefix", _GQA_SOURCES, "attn_gqa_parts_kernel", 512, 0, "shared"),
 }
 
 
@@ -142,6 +142,8 @@ def kernel_label(w, P, flags):
             and g <= 16 and not flags & 1)
     if P == PARTITION_BALANCED:
         return ("attn_gqa_balanced_kernel" if mfma else "attn_decode_balanced_kernel") + "+attn_reduce_balanced_kernel"
+    if mfma and P > 0 and len(w.batch) <= 4096:  # the persistent fixed-partition schedule
+        return "attn_gqa_parts_kernel+attn_gqa_reduce_parts_kernel"
     if mfma:
         return "attn_gqa_mfma_kernel" + ("+attn_gqa_reduce_kernel" if P > 0 else "")
     return "attn_decode_kernel" + ("+attn_reduce_kernel" if P > 0 else "")

@@ -238,7 +238,13 @@ int pkv_swap_blocks(const void *const *src_caches, void *const *dst_caches, int3
                     int32_t num_pairs, hipStream_t stream);
 
 /* Bytes of fp32 workspace a split mode needs:
- *  partition_size > 0: num_seqs * num_q_heads * ceil(max_context_len / partition_size) * (head_dim + 2) * 4;
+ *  partition_size > 0: R = num_seqs * num_q_heads * ceil(max_context_len / partition_size) partition
+ *                      rows of (head_dim + 2) floats. With head_dim 128, num_q_heads >= 2 and a
+ *                      device to query, room for the grouped-query kernel's persistent schedule
+ *                      follows: (align4(R * 130) + 8 * CU * min(num_q_heads, 16) * 130 + 4097
+ *                      + num_seqs * num_q_heads) * 4, CU = the current device's compute units
+ *                      (the rows padded to 16 bytes, one slot per wave and head of a group, the
+ *                      prefix sums, a flag per row). Otherwise R * (head_dim + 2) * 4;
  *  PKV_PARTITION_BALANCED: W * (2 * num_q_heads * (head_dim + 2) * 4 + 8) + 4097 * 4, where W is
  *                          2 * the current device's compute units (0 if the device cannot be queried);
  *  partition_size == 0: 0. */
@@ -256,8 +262,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *  context_lens:  device int32[num_seqs]; a sequence with length 0 gets zeros.
  *  max_context_len: host bound on context_lens, sizes the launch.
  *  partition_size: 0 = one pass per (sequence, head). > 0 (a multiple of block_size):
- *                 each (sequence, head) is cut into parts of that many tokens, computed
- *                 independently into workspace, then merged by a log-sum-exp reduce pass.
+ *                 each (sequence, head) is cut into parts of that many tokens, each part's
+ *                 attention computed on its own, then the parts merged by log-sum-exp. The
+ *                 grouped-query matrix-core kernel (up to 4096 sequences) streams the parts on a
+ *                 persistent schedule and merges the parts of a row that one workgroup held
+ *                 whole in the same launch; other rows go through workspace to a merge pass.
+ *                 Its rounding then depends on the compute-unit count, as in the balanced mode.
  *                 PKV_PARTITION_BALANCED: the batch's tiles are shared out evenly (see above),
  *                 then the same kind of merge; rounding then depends on the device's
  *                 compute-unit count (results are still reproducible on one device).

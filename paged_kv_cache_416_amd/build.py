@@ -20,12 +20,17 @@ FLAGS = [
     "-ffp-contract=off",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# attention_gqa.hip: uniform branches keep their if/else shape. Structurized, a uniform choice
+# between two kinds of load (cached or non-temporal) gains a path through neither, and the
+# compiler then counts the fewest loads on every path: its waits also wait for the next tile's
+# loads, which drains the load pipeline once per tile.
+SOURCE_FLAGS = {"attention_gqa.hip": ["-mllvm", "-structurizecfg-skip-uniform-regions=true"]}
 SOURCES = ["errors.cpp", "validate.cpp", "sha256.cpp", "pool.cpp", "sim.cpp", "cache_ops.hip", "attention.hip", "attention_gqa.hip", "prefill.hip", "probe.hip"]
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = ["hipcc", *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc", *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode:

@@ -148,10 +148,37 @@ constexpr int kBalancedMaxSeqs = 4096;
 constexpr int kBalancedWgsPerCu = 2;
 constexpr int kXcds = 8;
 
+// Fixed partitions of the grouped-query kernel on the persistent schedule (attention_gqa.hip):
+// one workgroup of kGqaPartsWaves waves per CU, each wave an equal share of the tile list.
+// Its workspace: the partition rows every fixed-partition launch uses (acc [rows][D], then m
+// [rows], then l [rows], rows = num_seqs * num_q_heads * num_parts), padded to 16 bytes; then
+// one slot per (wave, query head of the group) for a piece of a partition cut by a share
+// boundary (acc [slots][D], m [slots], l [slots]); then the prefix sums C (kBalancedMaxSeqs + 1);
+// then one flag per work row (kv head, sequence): merged by the attention kernel.
+constexpr int kGqaPartsWaves = 8;
+constexpr int kGqaMaxGroup = 16;
+
+__host__ __device__ inline int64_t parts_slot_offset(int64_t ws_rows, int64_t head_dim) {
+    return (ws_rows * (head_dim + 2) + 3) / 4 * 4;
+}
+__host__ __device__ inline int64_t parts_slot_count(int64_t wgs, int64_t group) { return wgs * kGqaPartsWaves * group; }
+__host__ __device__ inline int64_t parts_prefix_offset(int64_t ws_rows, int64_t head_dim, int64_t slots) {
+    return parts_slot_offset(ws_rows, head_dim) + slots * (head_dim + 2);
+}
+__host__ __device__ inline size_t parts_workspace_bytes(int64_t ws_rows, int64_t head_dim, int64_t slots,
+                                                        int64_t work_rows) {
+    return static_cast<size_t>(parts_prefix_offset(ws_rows, head_dim, slots) + kBalancedMaxSeqs + 1 + work_rows) * 4;
+}
+
 __device__ inline int64_t balanced_begin(int64_t v, int64_t T, int64_t nwg) { return v * T / nwg; }
 
-// The share holding tile x (0 <= x < T).
-__device__ inline int64_t balanced_owner(int64_t x, int64_t T, int64_t nwg) { return ((x + 1) * nwg - 1) / T; }
+// The share holding tile x (0 <= x < T): floor(((x + 1) nwg - 1) / T), taken in double precision
+// (a 64-bit integer division is a long instruction sequence on the GPU). Exact while T nwg < 2^53:
+// the numerator converts exactly, the quotient is below nwg, so the rounded quotient is within
+// nwg 2^-53 of the true one, while a true quotient below an integer k is at most k - 1/T.
+__device__ inline int64_t balanced_owner(int64_t x, int64_t T, int64_t nwg) {
+    return static_cast<int64_t>(static_cast<double>((x + 1) * nwg - 1) / static_cast<double>(T));
+}
 
 __device__ inline int64_t balanced_virtual(int64_t g, int64_t nwg) {
     return nwg % kXcds == 0 ? (g % kXcds) * (nwg / kXcds) + g / kXcds : g;
@@ -171,9 +198,9 @@ __device__ inline int32_t *balanced_records(const AttnParams &p) {
 
 // C[s] = tiles per row of the sequences before s, for s = 0 .. S (LDS, all threads of the
 // block); lengths clamped as everywhere else. Ends with a barrier (except workgroup 0's copy
-// of C into the workspace, which the merge pass reads after this kernel).
+// of C to `out` in the workspace, which the merge pass reads after this kernel).
 template <int NT>
-__device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_t *part) {
+__device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_t *part, uint32_t *out) {
     const int t = threadIdx.x, S = p.num_seqs, TR = p.tile_rows;
     const int per = (S + NT - 1) / NT, s0 = t * per;
     uint32_t sum = 0;
@@ -196,10 +223,8 @@ __device__ inline void balanced_prefix(const AttnParams &p, uint32_t *C, uint32_
     if (t == NT - 1) C[S] = part[NT - 1];
     __syncthreads();
     // workgroup 0 leaves C in the workspace, after the slots, for the merge pass
-    if (blockIdx.x == 0) {
-        uint32_t *out = balanced_prefix_out(p);
+    if (blockIdx.x == 0)
         for (int i = t; i <= S; i += NT) out[i] = C[i];
-    }
 }
 
 // Decode step with the cache write: 16-byte chunk `chunk` of sequence s's new key and value rows

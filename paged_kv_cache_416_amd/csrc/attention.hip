@@ -353,7 +353,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ MhaLds<W, D> lds;
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
-    balanced_prefix<W * 64>(p, C, part);
+    balanced_prefix<W * 64>(p, C, part, balanced_prefix_out(p));
     balanced_zero_empty<E, D, W * 64>(p, C);
     balanced_walk<D, false>(p, C, [&](int s, int h, int ta, int tb, const Sink &sink) {
         constexpr int TR = Shape<E, D, B>::TR;
@@ -649,7 +649,15 @@ extern "C" size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_hea
     }
     if (partition_size <= 0) return 0;
     const int64_t parts = ceil_div(max_context_len, partition_size);
-    return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+    const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
+    const int cus = device_compute_units();
+    if (head_dim == 128 && num_q_heads >= 2 && cus > 0) {
+        // room for the grouped-query kernel's persistent schedule, for any group it may serve
+        const int64_t group = std::min<int64_t>(num_q_heads, kGqaMaxGroup);
+        return parts_workspace_bytes(rows, head_dim, parts_slot_count(cus, group),
+                                     static_cast<int64_t>(num_seqs) * num_q_heads);
+    }
+    return static_cast<size_t>(rows) * (head_dim + 2) * sizeof(float);
 }
 
 namespace pkv {

@@ -43,12 +43,11 @@ constexpr int kGqaWaves = 4;          // per-item schedule: two workgroups per C
 constexpr int kGqaBalancedWaves = 8;  // balanced schedule: one workgroup per CU (two waves per SIMD)
 constexpr int kGqaTiles = 1;   // tiles per stage
 constexpr int kGqaStages = 2;  // stages in flight + the one consumed
-constexpr int kMaxGroup = 16;
 
 template <int W>
 struct GqaLds {
-    float m[W][kMaxGroup], l[W][kMaxGroup];
-    float acc[W][kMaxGroup][128];
+    float m[W][kGqaMaxGroup], l[W][kGqaMaxGroup];
+    float acc[W][kGqaMaxGroup][128];
     u32x4 kt[W][16 * 16];  // each wave's K tile, 16 rows x 16 chunks, chunk positions swizzled by row
 };
 
@@ -362,12 +361,579 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     __shared__ GqaLds<W> lds;
     __shared__ uint32_t C[kBalancedMaxSeqs + 1];
     __shared__ uint32_t part[W * 64];
-    balanced_prefix<W * 64>(p, C, part);
+    balanced_prefix<W * 64>(p, C, part, balanced_prefix_out(p));
     balanced_zero_empty<E, 128, W * 64>(p, C);
     balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
         gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
+}
+
+// Fixed partitions on a persistent schedule: grid = balanced_wgs workgroups (one per CU) of
+// kGqaPartsWaves waves, and every wave of the grid takes an equal share of the balanced
+// schedule's tile list (work rows = (kv head, sequence), head-major; each XCD a contiguous run
+// of shares). A wave streams its share through one register ring, across partition and row
+// boundaries, and writes each piece of a partition (its tiles of that partition) as soon as the
+// piece's last tile is consumed: no barrier, and no wave waits for another. A piece that starts
+// at its partition's start goes to the partition's workspace row, as on the per-item grid; any
+// other piece starts at its wave's share start (a share boundary cut the partition) and goes to
+// the wave's slot, which the merge pass adds to the partition. The arithmetic per tile is
+// gqa_range's with U = 1.
+// Where head j of a finished piece goes: its destination code c is the partition row of the
+// group's head 0 (c >= 0; head j at row c + j * num_parts) or -(w + 1) for wave w's slot.
+__device__ inline void piece_dest(const AttnParams &p, int64_t c, int j, float *&pa, float *&pm, float *&pl) {
+    constexpr int D = 128;
+    if (c < 0) {
+        float *sl = p.ws + parts_slot_offset(p.ws_rows, D);
+        const int64_t nsl = parts_slot_count(p.balanced_wgs, p.group), r = (-c - 1) * p.group + j;
+        pa = sl + r * D;
+        pm = sl + nsl * D + r;
+        pl = sl + nsl * (D + 1) + r;
+    } else {
+        const int64_t r = c + static_cast<int64_t>(j) * p.num_parts;
+        pa = p.ws + r * D;
+        pm = p.ws + p.ws_rows * D + r;
+        pl = p.ws + p.ws_rows * (D + 1) + r;
+    }
+}
+
+// The workgroup's LDS pool of finished pieces: piece b is acc [G][128], m [G], l [G] at
+// piece + b * G * 130, with its destination code, first tile and work row beside it. A wave
+// claims a piece with an LDS atomic (`used` may pass cap: a piece that finds the pool full is
+// stored at once). The pool is emptied after the workgroup's last barrier.
+struct PiecePool {
+    float *piece;
+    int64_t *dst;     // destination code
+    int64_t *key;     // the piece's first tile in the list: pieces sort into tile order by it
+    int32_t *row;     // its work row (kv head * num_seqs + sequence)
+    int32_t *order;   // the pieces in tile order (filled after the last wave is done)
+    uint32_t *used;
+    uint32_t cap;
+    int32_t *nruns;   // after the last wave: runs of pieces of one row
+    uint32_t *need;   // after the last wave: per wave of the workgroup, its slot is written neutral
+};
+
+template <class E, int B, bool PAGED, int POL, int QL>
+__device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t v, int64_t nw, u32x4 *kt,
+                                 const PiecePool &pool) {
+    using M = Mfma<E>;
+    constexpr int D = 128;
+    constexpr int TR = 16;
+    constexpr int SPB = B / TR;
+    constexpr int ROWB = D * 2;
+    static_assert(B % TR == 0, "block_size must be a multiple of 16");
+
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int G = p.group, S_ = p.num_seqs, PT = p.partition_size / TR;
+    const int64_t Ctot = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(C[S_]));
+    const int64_t T = Ctot * p.num_kv_heads;
+    const int64_t xb = balanced_begin(v, T, nw), xe = balanced_begin(v + 1, T, nw);
+    // a wave's slot, neutral: the merge pass may read it when the wave has no cut piece
+    auto neutral_slot = [&]() {
+        for (int c = lane; c < G * 32; c += 64) {
+            float *pa, *pm, *pl;
+            piece_dest(p, -(v + 1), c >> 5, pa, pm, pl);
+            *reinterpret_cast<f32x4 *>(pa + (c & 31) * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if ((c & 31) == 0) {
+                *pm = -INFINITY;
+                *pl = 0.f;
+            }
+        }
+    };
+    if (xb >= xe) {
+        neutral_slot();
+        return;
+    }
+
+    // The issue cursor, all uniform: the next tile x; its row (sequence s, kv head kvh, first
+    // position row0, nrow tiles, ctx tokens, clen of them through the caches); its partition
+    // (index part in the row, positions [pbeg, pend)); its table entry. Partition boundaries
+    // advance by additions: only a share's first tile divides.
+    int64_t x = xb, row0 = 0, pbeg = 0, pend = 0;
+    int s = 0, kvh = 0, nrow = 0, ctx = 0, clen = 0, cpb = 0, part = 0;
+    TableEntry *trow = nullptr;
+    auto locate = [&]() {
+        kvh = static_cast<int>(x / Ctot);
+        const int64_t rem = x - kvh * Ctot;
+        int lo = 0, hi = S_;  // the largest lo with C[lo] <= rem, which has tiles (C[lo + 1] > rem)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(C[mid])) <= rem) lo = mid; else hi = mid;
+        }
+        s = lo;
+        const uint32_t c0 = __builtin_amdgcn_readfirstlane(C[s]);
+        row0 = kvh * Ctot + c0;
+        nrow = static_cast<int>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(C[s + 1])) - c0);
+        ctx = clamp_ctx(*(TableEntry *)(p.ctx_lens + s), p.ctx_cap);  // scalar loads, like the table's
+        clen = POL == kLoadSplit ? *(TableEntry *)(p.cached_lens + s) : 0;
+        if constexpr (PAGED) trow = (TableEntry *)(p.tables + static_cast<int64_t>(s) * p.max_blocks);
+        part = 0;
+        if (x != row0) part = static_cast<int>((x - row0) / PT);
+        pbeg = row0 + static_cast<int64_t>(part) * PT;
+        pend = min(row0 + nrow, pbeg + PT);
+    };
+    auto lookup = [&]() {
+        if constexpr (PAGED) cpb = trow[static_cast<int>(x - row0) / SPB];
+    };
+    locate();
+    lookup();
+
+    struct Stage {
+        u32x4 k[4], v[4];  // [i]: chunk n of row 4g + i
+        u32x4 q[QL];       // the group's query rows (16 bytes a lane each), loaded for a piece's
+                           // first tile (zeros otherwise)
+        int64_t dst;       // the partition's workspace row for the group's head 0
+        int64_t x;         // the tile's list position
+        int rowid;         // its work row: kvh * num_seqs + s
+        int rows;          // rows of the tile that count (0: none)
+        bool valid;        // a tile of the share (else a stand-in past its end)
+        bool first, last;  // the first / last tile of a piece
+        bool slot;         // (first) the piece goes to the wave's slot
+    };
+
+    // Every load is unconditional (exact wait counts) and goes through a buffer resource that
+    // ends at the tile's last counted row: rows past it, a stand-in and a rejected table entry
+    // read as zeros with no memory traffic, and the query loads of a tile that starts no piece
+    // move nothing.
+    const unsigned roff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n (K and V)
+    // the query loads: QL = ceil(G / 4) of them (16 bytes a lane, 1 KiB each), so that a tile
+    // adds few load instructions; the operand layout is made through LDS at a piece's first tile
+    auto issue = [&](Stage &S) {
+        const bool valid = x < xe;
+        const int jt = static_cast<int>(x - row0);
+        const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+        S.valid = valid;
+        S.dst = row_q0 * p.num_parts + part;
+        S.x = x;
+        S.rowid = kvh * S_ + s;
+        S.first = valid && (x == xb || x == pbeg);
+        S.slot = x == xb && x != pbeg;
+        S.last = valid && (x + 1 == xe || x + 1 == pend);
+        int64_t tile;
+        bool ok;
+        if constexpr (PAGED) {
+            ok = static_cast<uint32_t>(cpb) < p.num_blocks;  // 32-bit, so it stays a scalar compare
+            const int64_t blk = ok ? cpb : 0;
+            tile = ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
+        } else {
+            ok = true;
+            tile = ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
+        }
+        const int rows = valid && ok ? min(TR, ctx - jt * TR) : 0;
+        S.rows = rows;
+        const auto kr_ = tile_rsrc(static_cast<const char *>(p.k) + tile, rows * ROWB);
+        const auto vr_ = tile_rsrc(static_cast<const char *>(p.v) + tile, rows * ROWB);
+        if (POL == kLoadCached || (POL == kLoadSplit && jt * TR < clen)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S.k[i] = kv_buffer_load<false>(kr_, roff + i * ROWB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S.v[i] = kv_buffer_load<false>(vr_, roff + i * ROWB);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S.k[i] = kv_buffer_load<true>(kr_, roff + i * ROWB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S.v[i] = kv_buffer_load<true>(vr_, roff + i * ROWB);
+        }
+        const auto qr_ = tile_rsrc(static_cast<const char *>(p.q) + row_q0 * ROWB, S.first ? G * ROWB : 0);
+#pragma unroll
+        for (int u = 0; u < QL; ++u) S.q[u] = kv_buffer_load<false>(qr_, (u * 64 + lane) * 16);
+        if (valid) {
+            ++x;
+            if (x < xe) {
+                if (x == row0 + nrow) {
+                    locate();
+                } else if (x == pend) {
+                    ++part;
+                    pbeg = x;
+                    pend = min(row0 + nrow, x + PT);
+                }
+                lookup();
+            }
+        }
+    };
+
+    u32x4 qv[4];  // the current piece's query operand
+    float m = -INFINITY, lsum = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool to_slot = false;
+    int64_t pstart = 0;  // the current piece's first tile and work row
+    int prow = 0;
+
+    // A piece's result, unnormalised (acc, m, l of each of the G heads), into the workgroup's
+    // pool, written out after the last barrier: a store in the stream would hold up the wave's
+    // later loads until it is acknowledged, which under a saturated memory system takes about a
+    // full queue drain. Then the state starts over for the next piece.
+    auto finish = [&](const Stage &S) {
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const int64_t code = to_slot ? -(v + 1) : S.dst;
+        uint32_t b = 0;
+        if (lane == 0) b = atomicAdd(pool.used, 1u);
+        b = __builtin_amdgcn_readfirstlane(b);
+        // lane (n, g) holds d = 8 (4g + i) + j: columns 32g .. 32g + 31 of head n
+        if (b < pool.cap) {
+            float *pc = pool.piece + static_cast<int64_t>(b) * G * (D + 2);
+            if (n < G) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 *dst = reinterpret_cast<f32x4 *>(pc + n * D + 8 * (4 * g + i));
+                    dst[0] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+                    dst[1] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+                }
+                if (g == 0) {
+                    pc[G * D + n] = m;
+                    pc[G * (D + 1) + n] = lsum;
+                }
+            }
+            if (lane == 0) {
+                pool.dst[b] = code;
+                pool.key[b] = pstart;
+                pool.row[b] = prow;
+            }
+        } else if (n < G) {
+            float *pa, *pm, *pl;
+            piece_dest(p, code, n, pa, pm, pl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 *dst = reinterpret_cast<f32x4 *>(pa + 8 * (4 * g + i));
+                dst[0] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+                dst[1] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+            }
+            if (g == 0) {
+                *pm = m;
+                *pl = lsum;
+            }
+        }
+        m = -INFINITY;
+        lsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    auto consume = [&](Stage &S) {
+        if (S.first) {
+            // the rows through the wave's LDS tile (the tile is free between two consumes), read
+            // back as the operand: query head n, chunks 4 * kk + g; zero for n >= G
+#pragma unroll
+            for (int u = 0; u < QL; ++u) kt[u * 64 + lane] = S.q[u];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) qv[kk] = n < G ? kt[n * 16 + 4 * kk + g] : u32x4{0u, 0u, 0u, 0u};
+            to_slot = S.slot;
+            pstart = S.x;
+            prow = S.rowid;
+        }
+        // K operand through the wave's LDS tile (chunk c of row r at position c ^ r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            kt[r * 16 + (n ^ r)] = S.k[i];
+        }
+        u32x4 ka[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = kt[n * 16 + ((4 * kk + g) ^ n)];
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
+        float sc[4];
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = 4 * g + i < S.rows ? c[i] * p.scale_log2 : -INFINITY;
+            mloc = fmaxf(mloc, sc[i]);
+        }
+        mloc = max_over_lane_groups(mloc);
+        const float m_new = fmaxf(m, mloc);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m) != 0, 0)) {
+            const float alpha = fast_exp2(m - m_ref);
+            lsum *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+        }
+        const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
+        const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
+        const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
+        const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
+        const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
+        lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
+        const u32x2 ph = {h01, h23}, pr = {r01, r23};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int w = j >> 1;
+            const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[1], w), word(S.v[0], w), sel),
+                              __builtin_amdgcn_perm(word(S.v[3], w), word(S.v[2], w), sel)};
+            acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
+        }
+        m = m_new;
+        if (S.last) finish(S);
+    };
+
+    // A ring of two stages: while one is consumed the other is in flight.
+    Stage R[2];
+    issue(R[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (;;) {
+        if (!R[0].valid) break;
+        issue(R[1]);
+        consume(R[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(R[0]);
+        consume(R[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// LDS of the persistent schedule: the waves' K tiles, the prefix sums C, then the piece pool.
+constexpr int kPartsLdsBytes = 160 * 1024;
+constexpr int kPartsKtBytes = kGqaPartsWaves * 16 * 16 * 16;
+
+// After the workgroup's last barrier: the pool's pieces in tile order. A work row whose tiles
+// all lie in this workgroup's tiles [X0, X1), with every piece in the pool, is merged here (the
+// partitions' merge, in tile order) and written to the output; the pieces of any other row go
+// to the workspace for the merge pass. flags[row] records which, for every row that starts in
+// [X0, X1); a wave of this workgroup whose share starts a partition of a row left to the merge
+// pass gets a neutral slot.
+template <class E>
+__device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const PiecePool &pool, int64_t vw0,
+                                   int64_t nw, int32_t *flags) {
+    constexpr int D = 128;
+    constexpr int TR = 16;
+    constexpr int NT = kGqaPartsWaves * 64;
+    const int G = p.group, S = p.num_seqs, PT = p.partition_size / TR;
+    const int64_t Ctot = C[S], T = Ctot * p.num_kv_heads;
+    const int64_t X0 = balanced_begin(vw0, T, nw), X1 = balanced_begin(vw0 + kGqaPartsWaves, T, nw);
+    const uint32_t used = *pool.used, np = min(used, pool.cap);
+    const bool spilled = used > pool.cap;  // pieces were stored at once: no row is merged here
+    // the row holding list position x (0 <= x < T)
+    auto locate = [&](int64_t x, int &r, int64_t &row0, int &nrow) {
+        const int kvh = static_cast<int>(x / Ctot);
+        const int64_t rem = x - kvh * Ctot;
+        int lo = 0, hi = S;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (C[mid] <= rem) lo = mid; else hi = mid;
+        }
+        r = kvh * S + lo;
+        row0 = kvh * Ctot + C[lo];
+        nrow = static_cast<int>(C[lo + 1] - C[lo]);
+    };
+    auto merged = [&](int64_t row0, int nrow) { return !spilled && row0 >= X0 && row0 + nrow <= X1; };
+    if (X0 >= X1) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t *need = pool.need;
+    int32_t &nruns = *pool.nruns;
+
+    // the pieces in tile order (their first tiles are distinct)
+    for (int b = threadIdx.x; b < static_cast<int>(np); b += NT) {
+        const int64_t k = pool.key[b];
+        int r = 0;
+        for (int b2 = 0; b2 < static_cast<int>(np); ++b2) r += pool.key[b2] < k;
+        pool.order[r] = b;
+    }
+    // flags of the rows that start here
+    {
+        int r0;
+        int64_t row0;
+        int nrow;
+        locate(X0, r0, row0, nrow);
+        if (row0 < X0) ++r0;  // the row holding X0 starts in an earlier workgroup
+        for (int r = r0 + threadIdx.x; r < p.num_kv_heads * S; r += NT) {
+            const int kvh = r / S, s = r - kvh * S;
+            const int64_t rs = kvh * Ctot + C[s];
+            if (rs >= X1) break;
+            flags[r] = merged(rs, static_cast<int>(C[s + 1] - C[s])) ? 1 : 0;
+        }
+    }
+    // the waves whose shares start a partition of a row that the merge pass takes
+    if (threadIdx.x < kGqaPartsWaves) {
+        const int64_t w = vw0 + threadIdx.x, xb = balanced_begin(w, T, nw);
+        bool nd = false;
+        if (xb < balanced_begin(w + 1, T, nw)) {
+            int r;
+            int64_t row0;
+            int nrow;
+            locate(xb, r, row0, nrow);
+            nd = (xb - row0) % PT == 0 && !merged(row0, nrow);
+        }
+        need[threadIdx.x] = nd;
+    }
+    __syncthreads();
+    // runs of pieces of one row: their starts in tile order (the keys' room is free now)
+    int32_t *runs = reinterpret_cast<int32_t *>(pool.key);
+    if (wave == 0) {
+        int nr = 0;
+        for (int base = 0; base < static_cast<int>(np); base += 64) {
+            const int i = base + lane;
+            const bool st = i < static_cast<int>(np) && (i == 0 || pool.row[pool.order[i]] != pool.row[pool.order[i - 1]]);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(st);
+            if (st) runs[nr + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = i;
+            nr += __builtin_popcountll(m);
+        }
+        if (lane == 0) {
+            runs[nr] = static_cast<int>(np);
+            nruns = nr;
+        }
+    }
+    for (int c = threadIdx.x; c < kGqaPartsWaves * G * 32; c += NT) {
+        const int w = c / (G * 32), cc = c - w * G * 32;
+        if (!need[w]) continue;
+        float *pa, *pm, *pl;
+        piece_dest(p, -(vw0 + w + 1), cc >> 5, pa, pm, pl);
+        *reinterpret_cast<f32x4 *>(pa + (cc & 31) * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if ((cc & 31) == 0) {
+            *pm = -INFINITY;
+            *pl = 0.f;
+        }
+    }
+    __syncthreads();
+    // each wave takes runs in turn: a row merged here goes to the output, any other row's pieces
+    // to the workspace; a lane holds 16 bytes (4 columns of one head)
+    for (int k = wave; k < nruns; k += kGqaPartsWaves) {
+        const int i0 = runs[k], i1 = runs[k + 1];
+        const int r = pool.row[pool.order[i0]];
+        const int kvh = r / S, s = r - kvh * S;
+        const int64_t row0 = kvh * Ctot + C[s];
+        if (merged(row0, static_cast<int>(C[s + 1] - C[s]))) {
+            const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+            for (int c = lane; c < G * 32; c += 64) {
+                const int hj = c >> 5;
+                float M = -INFINITY, L = 0.f;
+                f32x4 O = {0.f, 0.f, 0.f, 0.f};
+                for (int t = i0; t < i1; ++t) {
+                    const float *pc = pool.piece + static_cast<int64_t>(pool.order[t]) * G * (D + 2);
+                    const float mg = pc[G * D + hj], lg = pc[G * (D + 1) + hj];
+                    const f32x4 og = *reinterpret_cast<const f32x4 *>(pc + c * 4);
+                    const float Mn = fmaxf(M, mg);
+                    const float Mr = Mn == -INFINITY ? 0.f : Mn;
+                    const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
+                    L = fmaf(lg, f, L * a);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) O[e] = fmaf(og[e], f, O[e] * a);
+                    M = Mn;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) E::store(p.out, (row_q0 + hj) * D + (c & 31) * 4 + e, L > 0.f ? O[e] / L : 0.f);
+            }
+        } else {
+            for (int c = lane; c < (i1 - i0) * G * 32; c += 64) {
+                const int t = c / (G * 32), cc = c - t * G * 32, hj = cc >> 5;
+                const int b = pool.order[i0 + t];
+                const float *pc = pool.piece + static_cast<int64_t>(b) * G * (D + 2);
+                float *pa, *pm, *pl;
+                piece_dest(p, pool.dst[b], hj, pa, pm, pl);
+                *reinterpret_cast<f32x4 *>(pa + (cc & 31) * 4) = *reinterpret_cast<const f32x4 *>(pc + cc * 4);
+                if ((cc & 31) == 0) {
+                    *pm = pc[G * D + hj];
+                    *pl = pc[G * (D + 1) + hj];
+                }
+            }
+        }
+    }
+}
+
+template <class E, int B, bool PAGED, int POL, int QL>
+__global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_parts_kernel(
+    const AttnParams p) {
+    constexpr int D = 128;
+    constexpr int NT = kGqaPartsWaves * 64;
+    __shared__ __attribute__((aligned(16))) char smem[kPartsLdsBytes];
+    const int G = p.group;
+    const int cbytes = ((p.num_seqs + 1) * 4 + 15) / 16 * 16;
+    uint32_t *C = reinterpret_cast<uint32_t *>(smem + kPartsKtBytes);
+    char *rest = smem + kPartsKtBytes + cbytes;
+    // the pool: a 48-byte header (counter, run count, per-wave flags), then dst [cap], key [cap],
+    // row [cap], order [cap], then the pieces
+    static_assert(kGqaPartsWaves <= 10, "the pool header holds one flag per wave");
+    const uint32_t cap = static_cast<uint32_t>((kPartsLdsBytes - kPartsKtBytes - cbytes - 80) / (G * (D + 2) * 4 + 24));
+    char *q0 = rest + 48;
+    const PiecePool pool{reinterpret_cast<float *>(q0 + (cap * 24 + 15) / 16 * 16), reinterpret_cast<int64_t *>(q0),
+                         reinterpret_cast<int64_t *>(q0 + cap * 8), reinterpret_cast<int32_t *>(q0 + cap * 16),
+                         reinterpret_cast<int32_t *>(q0 + cap * 20), reinterpret_cast<uint32_t *>(rest), cap,
+                         reinterpret_cast<int32_t *>(rest + 4), reinterpret_cast<uint32_t *>(rest + 8)};
+    if (threadIdx.x == 0) *pool.used = 0u;
+    // the prefix scan's scratch sits where the pool will be (its last use precedes its last barrier)
+    const int64_t slots = parts_slot_count(p.balanced_wgs, G);
+    uint32_t *prefix = reinterpret_cast<uint32_t *>(p.ws + parts_prefix_offset(p.ws_rows, D, slots));
+    balanced_prefix<NT>(p, C, reinterpret_cast<uint32_t *>(q0), prefix);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nw = static_cast<int64_t>(p.balanced_wgs) * kGqaPartsWaves;
+    const int64_t vw0 = balanced_virtual(blockIdx.x, p.balanced_wgs) * kGqaPartsWaves;
+    gqa_share<E, B, PAGED, POL, QL>(p, C, vw0 + wave, nw, reinterpret_cast<u32x4 *>(smem) + wave * 256, pool);
+    __syncthreads();
+    parts_drain<E>(p, C, pool, vw0, nw, reinterpret_cast<int32_t *>(prefix + kBalancedMaxSeqs + 1));
+}
+
+// The merge pass of the persistent schedule, for the rows the attention kernel left to it (its
+// flags): grid = (num_kv_heads, num_seqs), 256 threads over
+// the group's G heads x 128 columns, one pass with a running maximum over the row's partitions
+// (their workspace rows), then over the slots of the waves whose shares begin inside the row
+// (owner of its first tile < w <= owner of its last: a cut piece of one of its partitions, or
+// neutral). The share boundaries depend only on the tile count.
+template <class E>
+__global__ __launch_bounds__(256) void attn_gqa_reduce_parts_kernel(const AttnParams p) {
+    constexpr int D = 128;
+    constexpr int TR = 16;
+    const int kvh = blockIdx.x, s = blockIdx.y, G = p.group;
+    const int64_t nsl = parts_slot_count(p.balanced_wgs, G);
+    const float *sl = p.ws + parts_slot_offset(p.ws_rows, D);
+    const uint32_t *C = reinterpret_cast<const uint32_t *>(p.ws + parts_prefix_offset(p.ws_rows, D, nsl));
+    // the three prefix sums first, so that their loads are in flight together
+    const uint32_t c0 = C[s], c1 = C[s + 1], cS = C[p.num_seqs];
+    const int32_t done = reinterpret_cast<const int32_t *>(C + kBalancedMaxSeqs + 1)[kvh * p.num_seqs + s];
+    const int64_t Ctot = cS, T = Ctot * p.num_kv_heads;
+    const int64_t nw = static_cast<int64_t>(p.balanced_wgs) * kGqaPartsWaves;
+    const int PT = p.partition_size / TR;
+    const int64_t row0 = kvh * Ctot + c0;
+    const int nrow = static_cast<int>(c1 - c0);
+    if (nrow > 0 && done) return;  // merged by the attention kernel
+    const int np = (nrow + PT - 1) / PT;
+    const int64_t w0 = nrow > 0 ? balanced_owner(row0, T, nw) + 1 : 0;
+    const int64_t w1 = nrow > 0 ? balanced_owner(row0 + nrow - 1, T, nw) : -1;
+    const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+        const int j = i / D, d = i % D;
+        float M = -INFINITY, L = 0.f, O = 0.f;
+        auto add = [&](float mg, float lg, float og) {
+            const float Mn = fmaxf(M, mg);
+            const float Mr = Mn == -INFINITY ? 0.f : Mn;
+            const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
+            L = fmaf(lg, f, L * a);
+            O = fmaf(og, f, O * a);
+            M = Mn;
+        };
+        const int64_t wr = (row_q0 + j) * p.num_parts;
+        const int total = np + static_cast<int>(w1 - w0 + 1);
+        // both kinds of piece in batches of 8: a batch's loads are issued together, then merged
+        // in order (a loop that runs its last iterations one by one waits a load latency for each)
+        constexpr int NB = 8;
+        for (int t0 = 0; t0 < total; t0 += NB) {
+            float mg[NB], lg[NB], og[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int t = t0 + u;
+                mg[u] = -INFINITY;
+                lg[u] = 0.f;
+                og[u] = 0.f;
+                if (t < total) {
+                    const bool row = t < np;
+                    const int64_t r = row ? wr + t : (w0 + t - np) * G + j;
+                    const float *base = row ? p.ws : sl;
+                    const int64_t rows = row ? p.ws_rows : nsl;
+                    mg[u] = base[rows * D + r];
+                    lg[u] = base[rows * (D + 1) + r];
+                    og[u] = base[r * D + d];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+                if (t0 + u < total) add(mg[u], lg[u], og[u]);
+        }
+        E::store(p.out, (row_q0 + j) * D + d, L > 0.f ? O / L : 0.f);
+    }
 }
 
 template <class E, int B, bool PAGED, int POL>
@@ -384,6 +950,35 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
                            dim3(q.balanced_wgs), dim3(kGqaBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "grouped-query attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
+    }
+    if (p.partition_size > 0) {
+        // fixed partitions: the persistent schedule where its limits and workspace allow
+        AttnParams q = p;
+        q.tile_rows = 16;
+        q.rows_per_seq = p.num_kv_heads;
+        q.heads_per_row = p.group;
+        q.head_major = 1;
+        const int cus = device_compute_units();
+        const int64_t tiles = static_cast<int64_t>(num_seqs) * ceil_div(p.ctx_cap, 16) * p.num_kv_heads;
+        if (cus > 0 && num_seqs <= kBalancedMaxSeqs && tiles < (int64_t(1) << 31) && q.ws &&
+            q.ws_bytes >= parts_workspace_bytes(q.ws_rows, 128, parts_slot_count(cus, q.group),
+                                                static_cast<int64_t>(num_seqs) * p.num_kv_heads)) {
+            q.balanced_wgs = cus;
+            if (q.group <= 4)
+                hipLaunchKernelGGL((attn_gqa_parts_kernel<E, B, PAGED, POL, 1>), dim3(cus), dim3(kGqaPartsWaves * 64),
+                                   0, stream, q);
+            else if (q.group <= 8)
+                hipLaunchKernelGGL((attn_gqa_parts_kernel<E, B, PAGED, POL, 2>), dim3(cus), dim3(kGqaPartsWaves * 64),
+                                   0, stream, q);
+            else
+                hipLaunchKernelGGL((attn_gqa_parts_kernel<E, B, PAGED, POL, 4>), dim3(cus), dim3(kGqaPartsWaves * 64),
+                                   0, stream, q);
+            int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
+            if (rc) return rc;
+            hipLaunchKernelGGL((attn_gqa_reduce_parts_kernel<E>), dim3(p.num_kv_heads, num_seqs), dim3(256), 0, stream,
+                               q);
+            return hip_status(hipGetLastError(), "grouped-query reduce launch");
+        }
     }
     hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, POL>),
                        dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
@@ -415,7 +1010,7 @@ int launch_block(const AttnParams &p, int32_t block_size, int pol, int32_t num_s
 
 bool gqa_mfma_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
     return (dtype == PKV_F16 || dtype == PKV_BF16) && head_dim == 128 && (block_size == 16 || block_size == 32) &&
-           group >= 2 && group <= kMaxGroup;
+           group >= 2 && group <= kGqaMaxGroup;
 }
 
 int launch_gqa_mfma(const AttnParams &p, int32_t dtype, int32_t block_size, bool paged, int load_policy,

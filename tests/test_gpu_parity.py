@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth
 from paged_kv_cache_416_amd import kernels
-from paged_kv_cache_416_amd._lib import PKV_EUNSUPPORTED, PkvError
+from paged_kv_cache_416_amd._lib import PKV_EINVAL, PKV_EUNSUPPORTED, PkvError
 from paged_kv_cache_416_amd.cache import PagedKVCache, poison_, to_device
 
 from harness import (TORCH_DTYPE, assert_close, cache_bytes, gpu_attention, gpu_replay, host_bytes, same_bytes, say,
@@ -382,6 +382,49 @@ def test_fixed_partitions_ragged_and_many(dtype, hq, hkv, lengths, parts):
         err = assert_close(out, ref, dtype, f"parts P={P}")
         assert bits_equal(gpu_attention(c, w, partition_size=P), out), "a second call differs"
         say(f"  P={P} max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("bf16", 16, 4), ("f16", 32, 4)])
+def test_fixed_partitions_both_schedules(dtype, hq, hkv):
+    """Grouped-query fixed partitions run on the persistent schedule up to 4096 sequences and on
+    the per-item grid past that; both match the oracle and repeat bit for bit. The persistent
+    schedule's workspace (partition rows, then slots, prefix sums and row flags) is what
+    pkv_decode_workspace_bytes asks for: the partition rows alone are refused."""
+    r = np.random.default_rng(91)
+    lens = r.integers(1, 700, size=24)
+    lens[3] = 2600
+    w = synth.decode_workload("schedules", 39, lens, hq, hkv, 128, 16, dtype, 0.5, 0.5)
+    st = oracle.replay(w)
+    ref = oracle.attention_of(st, w)
+    c = gpu_replay(w)
+    dt = TORCH_DTYPE[dtype]
+    q = to_device(w.q, dt, c.device)
+    tb, ctx, mx = c.tables(w.batch)
+    S, d = q.shape[0], q.shape[2]
+    for P in (16, 512):
+        parts = -(-mx // P)
+        rows_only = S * hq * parts * (d + 2) * 4
+        full = kernels.decode_workspace_bytes(S, hq, d, mx, P)
+        assert full > rows_only, "the persistent schedule's slots and flags need more room"
+        ws = torch.empty(full // 4 + 1, dtype=torch.float32, device=c.device)
+        out = torch.full_like(q, float("nan"))
+        kernels.paged_attention_decode(out, q, c.k, c.v, tb, ctx, mx, w.scale, P, ws)
+        again = torch.full_like(q, float("nan"))
+        kernels.paged_attention_decode(again, q, c.k, c.v, tb, ctx, mx, w.scale, P, ws)
+        torch.cuda.synchronize()
+        err = assert_close(out, ref, dtype, f"P={P}")
+        assert bits_equal(out, again), f"P={P}: a second call differs"
+        say(f"[schedules {dtype} Hq={hq} Hkv={hkv} P={P}] max abs err {err:.3e}")
+        small = torch.empty(rows_only // 4, dtype=torch.float32, device=c.device)
+        with pytest.raises(PkvError) as e:
+            kernels.paged_attention_decode(out, q, c.k, c.v, tb, ctx, mx, w.scale, P, small)
+        assert e.value.code == PKV_EINVAL
+    # past 4096 sequences: the per-item grid
+    lens2 = r.integers(1, 60, size=4097)
+    w2 = synth.decode_workload("schedules-4097", 40, lens2, hq, hkv, 128, 16, dtype, 0.5, 0.5)
+    ref2 = oracle.attention_of(oracle.replay(w2), w2)
+    c2 = gpu_replay(w2)
+    assert_close(gpu_attention(c2, w2, partition_size=32), ref2, dtype, "4097 sequences P=32")
 
 
 @pytest.mark.parametrize("one_launch", [False, True])
