@@ -42,7 +42,9 @@ struct PrefillParams {
 // stay in flight across the barrier)
 constexpr int kWaitLgkm0 = 0xC07F;
 
-template <class E, int B, int W, int RT>
+// POS: the scale is positive, so the maximum of the scaled logits is the scale times the
+// maximum of the raw ones, and each weight's exponent is one fma of its raw logit.
+template <class E, int B, int W, int RT, bool POS>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const PrefillParams p) {
     using M = Mfma<E>;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        sc[rt][u][i] = c[rt][u][i] * p.scale_log2;
+                        sc[rt][u][i] = POS ? c[rt][u][i] : c[rt][u][i] * p.scale_log2;
                         mloc[rt] = fmaxf(mloc[rt], sc[rt][u][i]);
                     }
             }
@@ -208,7 +210,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int kpos = t * kStepKeys + u * TR + 4 * g + i;  // qpos < kend: kend is implied
-                        sc[rt][u][i] = ok[u] && kpos <= qpos[rt] ? c[rt][u][i] * p.scale_log2 : -INFINITY;
+                        const float x = POS ? c[rt][u][i] : c[rt][u][i] * p.scale_log2;
+                        sc[rt][u][i] = ok[u] && kpos <= qpos[rt] ? x : -INFINITY;
                         mloc[rt] = fmaxf(mloc[rt], sc[rt][u][i]);
                     }
             }
@@ -221,7 +224,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         bool grow = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            m_new[rt] = fmaxf(m[rt], max_over_lane_groups(mloc[rt]));
+            const float mx = max_over_lane_groups(mloc[rt]);
+            m_new[rt] = fmaxf(m[rt], POS ? mx * p.scale_log2 : mx);
             grow = grow || m_new[rt] > m[rt] + kMaxSlack;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -244,7 +248,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    const float e0 = fast_exp2(sc[rt][u][2 * w] - m_ref), e1 = fast_exp2(sc[rt][u][2 * w + 1] - m_ref);
+                    const float a0 = sc[rt][u][2 * w], a1 = sc[rt][u][2 * w + 1];
+                    const float e0 = fast_exp2(POS ? fmaf(a0, p.scale_log2, -m_ref) : a0 - m_ref);
+                    const float e1 = fast_exp2(POS ? fmaf(a1, p.scale_log2, -m_ref) : a1 - m_ref);
                     const unsigned hw = M::pack2(e0, e1);
                     h[2 * u + w] = hw;
                     r[2 * u + w] = M::pack2(e0 - M::value(hw & 0xffffu), e1 - M::value(hw >> 16));
@@ -255,6 +261,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
             // the weight sums on the matrix cores: an all-ones operand in place of V^T gives
             // every row of the product the column sum of P^T, the same fp32 accumulation
             lsum[rt] = M::mma(kOnes, pr, M::mma(kOnes, ph, lsum[rt]));
+        }
+        // the first row tile's weighted sum beside the second's weights: its 18 MFMAs among the
+        // second tile's vector instructions
+        __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+#pragma unroll
+        for (int i = 0; i < 18; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
     };
 
@@ -317,9 +331,13 @@ int launch(const PrefillParams &p, int32_t max_query_len, int32_t num_seqs, hipS
     // dispatched in linear order, so every (kv head, sequence) pair's last rows, which need the
     // most keys, go first, and the light first rows of all pairs fill in at the end (longest
     // first). The kv head fastest deals each kv head to one XCD, whose L2 then holds its keys.
-    hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles>),
-                       dim3(p.num_kv_heads, num_seqs, static_cast<unsigned>(gz)), dim3(kPrefillWaves * 64), 0, stream,
-                       p);
+    const dim3 grid(p.num_kv_heads, num_seqs, static_cast<unsigned>(gz));
+    if (p.scale_log2 > 0.f)
+        hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles, true>), grid, dim3(kPrefillWaves * 64),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<E, B, kPrefillWaves, kPrefillRowTiles, false>), grid, dim3(kPrefillWaves * 64),
+                           0, stream, p);
     return hip_status(hipGetLastError(), "pkv_paged_attention_prefill launch");
 }
 
