@@ -41,7 +41,6 @@ namespace {
 
 constexpr int kGqaWaves = 4;          // per-item schedule: two workgroups per CU
 constexpr int kGqaBalancedWaves = 8;  // balanced schedule: one workgroup per CU (two waves per SIMD)
-constexpr int kGqaTiles = 1;   // tiles per stage
 constexpr int kGqaStages = 2;  // stages in flight + the one consumed
 
 template <int W>
@@ -52,18 +51,82 @@ struct GqaLds {
 };
 
 
+// One 16-row tile's contribution to the running softmax state (max m, weight sum lsum, Oᵀ
+// accumulators) of the group's heads. kr / vr: the tile's K and V rows as loaded (load i: chunk
+// n of row 4g + i); rows 0 .. rows - 1 count, the rest are masked out (rows <= 0: none). The K
+// rows reach the A-operand layout through the wave's LDS tile kt (a wave's LDS operations
+// complete in order, so the reads see the writes and the next tile's writes follow them).
+template <class E>
+__device__ inline void gqa_tile(const u32x4 (&kr)[4], const u32x4 (&vr)[4], const u32x4 (&qv)[4], int rows,
+                                float scale_log2, u32x4 *kt, float &m, float &lsum, f32x4 (&acc)[8]) {
+    using M = Mfma<E>;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g = lane >> 4;
+    // K operand: chunk c of row r at position c ^ r of the row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        kt[r * 16 + (n ^ r)] = kr[i];
+    }
+    u32x4 ka[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ka[kk] = kt[n * 16 + ((4 * kk + g) ^ n)];
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
+    float sc[4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sc[i] = 4 * g + i < rows ? c[i] * scale_log2 : -INFINITY;
+        mloc = fmaxf(mloc, sc[i]);
+    }
+    // the head's running max over its four lane groups (lanes n, n+16, n+32, n+48)
+    mloc = max_over_lane_groups(mloc);
+    const float m_new = fmaxf(m, mloc);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    // rescale only when some head's max moved: rare after the first tiles (uniform branch)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m) != 0, 0)) {
+        const float alpha = fast_exp2(m - m_ref);
+        lsum *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    }
+    // P^T operand: head n, tokens 4g .. 4g+3. The matrix cores take 16-bit operands, so each
+    // weight goes in as a 16-bit part plus the 16-bit rounding of its remainder (the remainder of
+    // a round to nearest is exact in fp32): two contractions see the fp32 weight to about 2^-16
+    // relative. The sum l takes the same parts (a dot2 with (1, 1) per pair).
+    const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
+    const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
+    const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
+    const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
+    const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
+    lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
+    const u32x2 ph = {h01, h23}, pr = {r01, r23};
+    // (a masked row reads as zeros and its weight is zero)
+    // V^T operand of MFMA j: element j of the lane's 4 V rows
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 vt = {__builtin_amdgcn_perm(word(vr[1], w), word(vr[0], w), sel),
+                          __builtin_amdgcn_perm(word(vr[3], w), word(vr[2], w), sel)};
+        acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
+    }
+    m = m_new;
+}
+
 // Tokens [t0, t1) of sequence s for kv head kvh and its G query heads (t0 a multiple of 16,
 // t0 < t1 <= the length): the workgroup's merged result goes to sink. Uniform over the
 // workgroup; ends with a barrier, so the caller may run it again on the same LDS. head_dim 128,
 // 16-bit types.
 //
-// The range's tiles go to the waves in stages of U tiles, round-robin. Each wave keeps NS
-// stages in registers: while it consumes one, the next NS - 1 are in flight, and the table
-// entries of the stage after those are on the way.
-template <class E, int B, bool PAGED, int W, int U, int POL>
+// The range's tiles go to the waves round-robin, one tile a stage. Each wave keeps NS stages in
+// registers: while it consumes one, the next NS - 1 are in flight, and the table entry of the
+// stage after those is on the way.
+template <class E, int B, bool PAGED, int W, int POL>
 __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, int t1, const Sink &sink,
                                  GqaLds<W> &lds) {
-    using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;          // tile rows
     constexpr int SPB = B / TR;     // tiles per block
@@ -77,7 +140,6 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     const int n = lane & 15, g = lane >> 4;
     const int jt0 = t0 / TR;
     const int ntile = (t1 + TR - 1) / TR - jt0;
-    const int nstage = (ntile + U - 1) / U;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
     TableEntry *trow = PAGED ? (TableEntry *)(p.tables + static_cast<int64_t>(s) * p.max_blocks)  // address-space cast
                              : nullptr;
@@ -96,58 +158,51 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     // tokens below clen are loaded through the caches (uniform: a scalar compare per tile)
     const int clen = POL == kLoadSplit ? __builtin_amdgcn_readfirstlane(p.cached_lens[s]) : 0;
 
-    // the next stage this wave will issue (wave w takes stages w, w + W, w + 2W, ...: a fixed
-    // assignment, so the summation order and the result do not depend on timing) and its
-    // table entries, looked up one stage ahead
+    // the next tile this wave will issue (wave w takes tiles w, w + W, w + 2W, ...: a fixed
+    // assignment, so the summation order and the result do not depend on timing) and its table
+    // entry, looked up one stage ahead
     int cst = wave;
-    int cpb[U];
+    int cpb = 0;
     auto lookup = [&]() {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = min(cst * U + u, ntile - 1);  // a stand-in past the range reads the last entry
-            cpb[u] = PAGED ? trow[(jt0 + k) / SPB] : 0;
-        }
+        const int k = min(cst, ntile - 1);  // a stand-in past the range reads the last entry
+        cpb = PAGED ? trow[(jt0 + k) / SPB] : 0;
     };
     lookup();
 
     struct Stage {
-        u32x4 k[U][4], v[U][4];  // [i]: chunk n of row 4g + i
-        int st;      // stage index within the range (>= nstage: a stand-in)
-        bool ok[U];  // table entry inside the pool
+        u32x4 k[4], v[4];  // [i]: chunk n of row 4g + i
+        int st;   // tile index within the range (>= ntile: a stand-in)
+        bool ok;  // table entry inside the pool
     };
 
     // Every load is unconditional (exact wait counts) and goes through a buffer resource that
     // ends at the tile's last row inside [t0, t1): rows past it, a stand-in tile and a tile whose
-    // table entry is rejected read as zeros, with no memory traffic; consume() masks them out.
+    // table entry is rejected read as zeros, with no memory traffic; the tile update masks them.
     const unsigned roff = g * 4 * ROWB + n * 16;  // + i * ROWB: row 4g + i, chunk n (K and V)
     auto issue = [&](Stage &S) {
         S.st = cst;
+        const int jt = jt0 + min(cst, ntile - 1);
+        int64_t tile;
+        if constexpr (PAGED) {
+            S.ok = static_cast<uint32_t>(cpb) < p.num_blocks;  // 32-bit, so it stays a scalar compare
+            const int64_t blk = S.ok ? cpb : 0;
+            tile = ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
+        } else {
+            S.ok = true;
+            tile = ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
+        }
+        const int rows = cst < ntile && S.ok ? min(TR, t1 - (jt0 + cst) * TR) : 0;
+        const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
+        if (POL == kLoadCached || (POL == kLoadSplit && (jt0 + cst) * TR < clen)) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k = cst * U + u;
-            const int jt = jt0 + min(k, ntile - 1);
-            int64_t tile;
-            if constexpr (PAGED) {
-                S.ok[u] = static_cast<uint32_t>(cpb[u]) < p.num_blocks;  // 32-bit, so it stays a scalar compare
-                const int64_t blk = S.ok[u] ? cpb[u] : 0;
-                tile = ((blk * p.num_kv_heads + kvh) * B + (jt % SPB) * TR) * ROWB;
-            } else {
-                S.ok[u] = true;
-                tile = ((static_cast<int64_t>(s) * p.num_kv_heads + kvh) * p.lmax + static_cast<int64_t>(jt) * TR) * ROWB;
-            }
-            const int rows = k < ntile && S.ok[u] ? min(TR, t1 - (jt0 + k) * TR) : 0;
-            const auto kr_ = tile_rsrc(kc + tile, rows * ROWB), vr_ = tile_rsrc(vc + tile, rows * ROWB);
-            if (POL == kLoadCached || (POL == kLoadSplit && (jt0 + k) * TR < clen)) {
+            for (int i = 0; i < 4; ++i) S.k[i] = kv_buffer_load<false>(kr_, roff + i * ROWB);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<false>(kr_, roff + i * ROWB);
+            for (int i = 0; i < 4; ++i) S.v[i] = kv_buffer_load<false>(vr_, roff + i * ROWB);
+        } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<false>(vr_, roff + i * ROWB);
-            } else {
+            for (int i = 0; i < 4; ++i) S.k[i] = kv_buffer_load<true>(kr_, roff + i * ROWB);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S.k[u][i] = kv_buffer_load<true>(kr_, roff + i * ROWB);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S.v[u][i] = kv_buffer_load<true>(vr_, roff + i * ROWB);
-            }
+            for (int i = 0; i < 4; ++i) S.v[i] = kv_buffer_load<true>(vr_, roff + i * ROWB);
         }
         cst += W;
         lookup();
@@ -157,75 +212,11 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     f32x4 acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // The K tile in the A-operand layout: through the wave's LDS tile (a wave's LDS operations
-    // complete in order, so a tile's reads see its writes and the next tile's writes follow them).
     u32x4 *kt = lds.kt[wave];
-    auto k_operand = [&](const u32x4 (&rows)[4], u32x4 (&ka)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            kt[r * 16 + (n ^ r)] = rows[i];
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[kk] = kt[n * 16 + ((4 * kk + g) ^ n)];
-    };
-
     auto consume = [&](Stage &S) {
-        float sc[U][4];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 ka[4];
-            k_operand(S.k[u], ka);
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
-            const int tok0 = (jt0 + S.st * U + u) * TR;  // a stand-in's rows all lie past t1
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool valid = S.ok[u] && tok0 + 4 * g + i < t1;
-                sc[u][i] = valid ? c[i] * p.scale_log2 : -INFINITY;
-                mloc = fmaxf(mloc, sc[u][i]);
-            }
-        }
-        // the head's running max over its four lane groups (lanes n, n+16, n+32, n+48)
-        mloc = max_over_lane_groups(mloc);
-        const float m_new = fmaxf(m, mloc);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        // rescale only when some head's max moved: rare after the first tiles (uniform branch)
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m) != 0, 0)) {
-            const float alpha = fast_exp2(m - m_ref);
-            lsum *= alpha;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            // P^T operand: head n, tokens 4g .. 4g+3 of tile u. The matrix cores take 16-bit
-            // operands, so each weight goes in as a 16-bit part plus the 16-bit rounding of its
-            // remainder (the remainder of a round to nearest is exact in fp32): two contractions
-            // see the fp32 weight to about 2^-16 relative. The sum l takes the same parts (a dot2
-            // with (1, 1) per pair).
-            const float e0 = fast_exp2(sc[u][0] - m_ref), e1 = fast_exp2(sc[u][1] - m_ref);
-            const float e2 = fast_exp2(sc[u][2] - m_ref), e3 = fast_exp2(sc[u][3] - m_ref);
-            const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
-            const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
-            const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
-            lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
-            const u32x2 ph = {h01, h23}, pr = {r01, r23};
-            // (a rejected or stand-in tile reads as zeros and its weights are zero)
-            // V^T operand of MFMA j: element j of the lane's 4 V rows
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = j >> 1;
-                const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[u][1], w), word(S.v[u][0], w), sel),
-                                  __builtin_amdgcn_perm(word(S.v[u][3], w), word(S.v[u][2], w), sel)};
-                acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
-            }
-        }
-        m = m_new;
+        // a stand-in's rows all lie past t1
+        const int rows = S.ok ? t1 - (jt0 + S.st) * TR : 0;
+        gqa_tile<E>(S.k, S.v, qv, rows, p.scale_log2, kt, m, lsum, acc);
     };
 
     // A ring of NS stages; the wave stops once the oldest stage is past the range (its later
@@ -241,7 +232,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
     // rounds keep the compiler's wait counts exact. The last round may consume up to NS - 1
     // stand-ins (zeros, masked; their loads move no data).
     for (;;) {
-        if (R[0].st >= nstage) break;
+        if (R[0].st >= ntile) break;
 #pragma unroll
         for (int r = 0; r < NS; ++r) {
             issue(R[(r + NS - 1) % NS]);
@@ -294,7 +285,7 @@ __device__ inline void gqa_range(const AttnParams &p, int s, int kvh, int t0, in
 // so that a kv head's workgroups share XCDs (and the L2 holding a shared prefix). At most 256
 // registers per lane (two waves per SIMD): two workgroups share a CU and one's start-up hides
 // behind the other.
-template <class E, int B, bool PAGED, int W, int U, int POL>
+template <class E, int B, bool PAGED, int W, int POL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_mfma_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -315,7 +306,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         sink = Sink{p.ws + wr * 128, p.ws + p.ws_rows * 128 + wr, p.ws + p.ws_rows * 129 + wr,
                     static_cast<int64_t>(p.num_parts) * 128, p.num_parts};
     }
-    gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, t0, t1, sink, lds);
+    gqa_range<E, B, PAGED, W, POL>(p, s, kvh, t0, t1, sink, lds);
 }
 
 // The fixed-partition merge of one (sequence, kv head): grid = (num_kv_heads, num_seqs), the kv
@@ -355,7 +346,7 @@ __global__ __launch_bounds__(256) void attn_gqa_reduce_kernel(const AttnParams p
 // batch's tiles (work rows = (kv head, sequence), head-major); cut rows are merged by the
 // balanced reduce pass. One workgroup per CU because two sharing a CU do not progress at one
 // pace (the older one's waves are served first), and the later one would finish alone.
-template <class E, int B, bool PAGED, int W, int U, int POL>
+template <class E, int B, bool PAGED, int W, int POL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_gqa_balanced_kernel(
     const AttnParams p) {
     __shared__ GqaLds<W> lds;
@@ -365,7 +356,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
     balanced_zero_empty<E, 128, W * 64>(p, C);
     balanced_walk<128, true>(p, C, [&](int s, int kvh, int ta, int tb, const Sink &sink) {
         const int ctx = clamp_ctx(p.ctx_lens[s], p.ctx_cap);
-        gqa_range<E, B, PAGED, W, U, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
+        gqa_range<E, B, PAGED, W, POL>(p, s, kvh, ta * 16, min(tb * 16, ctx), sink, lds);
     });
 }
 
@@ -373,12 +364,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 // kGqaPartsWaves waves, and every wave of the grid takes an equal share of the balanced
 // schedule's tile list (work rows = (kv head, sequence), head-major; each XCD a contiguous run
 // of shares). A wave streams its share through one register ring, across partition and row
-// boundaries, and writes each piece of a partition (its tiles of that partition) as soon as the
-// piece's last tile is consumed: no barrier, and no wave waits for another. A piece that starts
-// at its partition's start goes to the partition's workspace row, as on the per-item grid; any
-// other piece starts at its wave's share start (a share boundary cut the partition) and goes to
-// the wave's slot, which the merge pass adds to the partition. The arithmetic per tile is
-// gqa_range's with U = 1.
+// boundaries, with no barrier: no wave waits for another. The tiles of one partition inside one
+// share form a piece, computed on its own. A piece that starts at its partition's start belongs
+// to the partition's workspace row, as on the per-item grid; any other piece starts at its
+// wave's share start (a share boundary cut the partition) and belongs to the wave's slot. A
+// finished piece goes to the workgroup's LDS pool, not to memory. After the workgroup's last
+// barrier, rows whose pieces all sit in the pool are merged there and written to the output,
+// and the pieces of the other rows go to the workspace for the merge pass.
+
 // Where head j of a finished piece goes: its destination code c is the partition row of the
 // group's head 0 (c >= 0; head j at row c + j * num_parts) or -(w + 1) for wave w's slot.
 __device__ inline void piece_dest(const AttnParams &p, int64_t c, int j, float *&pa, float *&pm, float *&pl) {
@@ -416,7 +409,6 @@ struct PiecePool {
 template <class E, int B, bool PAGED, int POL, int QL>
 __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t v, int64_t nw, u32x4 *kt,
                                  const PiecePool &pool) {
-    using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;
     constexpr int SPB = B / TR;
@@ -625,50 +617,7 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
             pstart = S.x;
             prow = S.rowid;
         }
-        // K operand through the wave's LDS tile (chunk c of row r at position c ^ r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            kt[r * 16 + (n ^ r)] = S.k[i];
-        }
-        u32x4 ka[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) ka[kk] = kt[n * 16 + ((4 * kk + g) ^ n)];
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) c = M::mma(ka[kk], qv[kk], c);
-        float sc[4];
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sc[i] = 4 * g + i < S.rows ? c[i] * p.scale_log2 : -INFINITY;
-            mloc = fmaxf(mloc, sc[i]);
-        }
-        mloc = max_over_lane_groups(mloc);
-        const float m_new = fmaxf(m, mloc);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        if (__builtin_expect(__builtin_amdgcn_ballot_w64(m_new > m) != 0, 0)) {
-            const float alpha = fast_exp2(m - m_ref);
-            lsum *= alpha;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-        }
-        const float e0 = fast_exp2(sc[0] - m_ref), e1 = fast_exp2(sc[1] - m_ref);
-        const float e2 = fast_exp2(sc[2] - m_ref), e3 = fast_exp2(sc[3] - m_ref);
-        const unsigned h01 = M::pack2(e0, e1), h23 = M::pack2(e2, e3);
-        const unsigned r01 = M::pack2(e0 - M::value(h01 & 0xffffu), e1 - M::value(h01 >> 16));
-        const unsigned r23 = M::pack2(e2 - M::value(h23 & 0xffffu), e3 - M::value(h23 >> 16));
-        lsum = M::sum2(r23, M::sum2(r01, M::sum2(h23, M::sum2(h01, lsum))));
-        const u32x2 ph = {h01, h23}, pr = {r01, r23};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int w = j >> 1;
-            const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
-            const u32x2 vt = {__builtin_amdgcn_perm(word(S.v[1], w), word(S.v[0], w), sel),
-                              __builtin_amdgcn_perm(word(S.v[3], w), word(S.v[2], w), sel)};
-            acc[j] = M::mma16(vt, pr, M::mma16(vt, ph, acc[j]));
-        }
-        m = m_new;
+        gqa_tile<E>(S.k, S.v, qv, S.rows, p.scale_log2, kt, m, lsum, acc);
         if (S.last) finish(S);
     };
 
@@ -946,7 +895,7 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
         q.head_major = 1;  // an XCD's shares cover few kv heads: shared blocks stay in its L2
         int rc = balanced_check(q, 1);  // one workgroup per CU: two per CU would not run at one pace
         if (rc) return rc;
-        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaBalancedWaves, kGqaTiles, POL>),
+        hipLaunchKernelGGL((attn_gqa_balanced_kernel<E, B, PAGED, kGqaBalancedWaves, POL>),
                            dim3(q.balanced_wgs), dim3(kGqaBalancedWaves * 64), 0, stream, q);
         rc = hip_status(hipGetLastError(), "grouped-query attention launch");
         return rc ? rc : launch_reduce_balanced(q, E::CODE, 128, stream);
@@ -980,7 +929,7 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
             return hip_status(hipGetLastError(), "grouped-query reduce launch");
         }
     }
-    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, kGqaTiles, POL>),
+    hipLaunchKernelGGL((attn_gqa_mfma_kernel<E, B, PAGED, kGqaWaves, POL>),
                        dim3(p.num_kv_heads, grid_parts, num_seqs), dim3(kGqaWaves * 64), 0, stream, p);
     int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
     if (rc || p.partition_size <= 0) return rc;
