@@ -256,7 +256,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   for each sequence s and query head h (kv head h / (num_q_heads/num_kv_heads)):
  *   out[s][h] = softmax_t(scale * q[s][h] . K_t) . V_t over t < context_lens[s],
  *   K_t, V_t read from block block_tables[s][t / block_size], row t % block_size.
- *  out, q:        [num_seqs][num_q_heads][head_dim]; out is written in dtype (RNE).
+ *  out, q:        device [num_seqs][num_q_heads][head_dim], 16-byte aligned; out is written in
+ *                 dtype (RNE).
  *  block_tables:  device int32[num_seqs][max_blocks_per_seq]; entries past a sequence's
  *                 last block are never read (so they may hold anything).
  *  context_lens:  device int32[num_seqs]; a sequence with length 0 gets zeros.

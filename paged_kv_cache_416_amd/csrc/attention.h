@@ -170,7 +170,13 @@ __host__ __device__ inline size_t parts_workspace_bytes(int64_t ws_rows, int64_t
     return static_cast<size_t>(parts_prefix_offset(ws_rows, head_dim, slots) + kBalancedMaxSeqs + 1 + work_rows) * 4;
 }
 
-__device__ inline int64_t balanced_begin(int64_t v, int64_t T, int64_t nwg) { return v * T / nwg; }
+// floor(v T / nwg) in double precision (a 64-bit integer division is a long instruction sequence
+// on the GPU). Exact while v T < 2^53 (v <= nwg < 2^20, T < 2^31): a quotient that is an integer is
+// represented exactly, and any other lies at least 1 / nwg from the integers, more than the
+// rounding error q 2^-53 < 2^-22.
+__device__ inline int64_t balanced_begin(int64_t v, int64_t T, int64_t nwg) {
+    return static_cast<int64_t>(static_cast<double>(v * T) / static_cast<double>(nwg));
+}
 
 // The share holding tile x (0 <= x < T): floor(((x + 1) nwg - 1) / T), taken in double precision
 // (a 64-bit integer division is a long instruction sequence on the GPU). Exact while T nwg < 2^53:

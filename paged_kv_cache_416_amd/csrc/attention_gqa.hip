@@ -397,18 +397,21 @@ __device__ inline void piece_dest(const AttnParams &p, int64_t c, int j, float *
 struct PiecePool {
     float *piece;
     int64_t *dst;     // destination code
-    int64_t *key;     // the piece's first tile in the list: pieces sort into tile order by it
+    int32_t *key;     // wave * 65536 + the piece's index among the wave's pieces (tile order);
+                      // cap + 1 entries
     int32_t *row;     // its work row (kv head * num_seqs + sequence)
     int32_t *order;   // the pieces in tile order (filled after the last wave is done)
     uint32_t *used;
     uint32_t cap;
     int32_t *nruns;   // after the last wave: runs of pieces of one row
     uint32_t *need;   // after the last wave: per wave of the workgroup, its slot is written neutral
+    uint32_t *count;  // per wave of the workgroup: its pieces
 };
 
+// Returns the number of pieces the wave finished (uniform).
 template <class E, int B, bool PAGED, int POL, int QL>
-__device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t v, int64_t nw, u32x4 *kt,
-                                 const PiecePool &pool) {
+__device__ inline int gqa_share(const AttnParams &p, const uint32_t *C, int64_t v, int64_t nw, u32x4 *kt,
+                                const PiecePool &pool) {
     constexpr int D = 128;
     constexpr int TR = 16;
     constexpr int SPB = B / TR;
@@ -435,7 +438,7 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
     };
     if (xb >= xe) {
         neutral_slot();
-        return;
+        return 0;
     }
 
     // The issue cursor, all uniform: the next tile x; its row (sequence s, kv head kvh, first
@@ -476,7 +479,6 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
         u32x4 q[QL];       // the group's query rows (16 bytes a lane each), loaded for a piece's
                            // first tile (zeros otherwise)
         int64_t dst;       // the partition's workspace row for the group's head 0
-        int64_t x;         // the tile's list position
         int rowid;         // its work row: kvh * num_seqs + s
         int rows;          // rows of the tile that count (0: none)
         bool valid;        // a tile of the share (else a stand-in past its end)
@@ -497,7 +499,6 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
         const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
         S.valid = valid;
         S.dst = row_q0 * p.num_parts + part;
-        S.x = x;
         S.rowid = kvh * S_ + s;
         S.first = valid && (x == xb || x == pbeg);
         S.slot = x == xb && x != pbeg;
@@ -551,8 +552,8 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool to_slot = false;
-    int64_t pstart = 0;  // the current piece's first tile and work row
-    int prow = 0;
+    int prow = 0;        // the current piece's work row
+    int npieces = 0;     // pieces finished so far
 
     // A piece's result, unnormalised (acc, m, l of each of the G heads), into the workgroup's
     // pool, written out after the last barrier: a store in the stream would hold up the wave's
@@ -582,7 +583,7 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
             }
             if (lane == 0) {
                 pool.dst[b] = code;
-                pool.key[b] = pstart;
+                pool.key[b] = static_cast<int32_t>(threadIdx.x >> 6) * 65536 + npieces;
                 pool.row[b] = prow;
             }
         } else if (n < G) {
@@ -603,6 +604,7 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
         lsum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ++npieces;
     };
 
     auto consume = [&](Stage &S) {
@@ -614,7 +616,6 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) qv[kk] = n < G ? kt[n * 16 + 4 * kk + g] : u32x4{0u, 0u, 0u, 0u};
             to_slot = S.slot;
-            pstart = S.x;
             prow = S.rowid;
         }
         gqa_tile<E>(S.k, S.v, qv, S.rows, p.scale_log2, kt, m, lsum, acc);
@@ -634,29 +635,36 @@ __device__ inline void gqa_share(const AttnParams &p, const uint32_t *C, int64_t
         consume(R[1]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    return npieces;
 }
 
 // LDS of the persistent schedule: the waves' K tiles, the prefix sums C, then the piece pool.
 constexpr int kPartsLdsBytes = 160 * 1024;
 constexpr int kPartsKtBytes = kGqaPartsWaves * 16 * 16 * 16;
 
-// After the workgroup's last barrier: the pool's pieces in tile order. A work row whose tiles
-// all lie in this workgroup's tiles [X0, X1), with every piece in the pool, is merged here (the
-// partitions' merge, in tile order) and written to the output; the pieces of any other row go
-// to the workspace for the merge pass. flags[row] records which, for every row that starts in
+// After the workgroup's last wave is done: the pool's pieces in tile order (a wave's pieces are
+// in tile order and the waves' shares follow one another, so a piece's place is the count of
+// the earlier waves' pieces plus its index). A work row whose tiles all lie in this
+// workgroup's tiles [X0, X1), with every piece in the pool, is merged here (the partitions'
+// merge, in tile order) and written to the output; the pieces of any other row go to the
+// workspace for the merge pass. flags[row] records which, for every row that starts in
 // [X0, X1); a wave of this workgroup whose share starts a partition of a row left to the merge
-// pass gets a neutral slot.
+// pass gets a neutral slot. The LDS work comes first, behind LDS-only barriers; every global
+// write comes after the last barrier (a block barrier would also wait for stores to complete).
 template <class E>
 __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const PiecePool &pool, int64_t vw0,
                                    int64_t nw, int32_t *flags) {
+    using M = Mfma<E>;
     constexpr int D = 128;
     constexpr int TR = 16;
     constexpr int NT = kGqaPartsWaves * 64;
+    constexpr int NB = 8;  // pieces whose loads are in flight together while a row is merged
     const int G = p.group, S = p.num_seqs, PT = p.partition_size / TR;
     const int64_t Ctot = C[S], T = Ctot * p.num_kv_heads;
     const int64_t X0 = balanced_begin(vw0, T, nw), X1 = balanced_begin(vw0 + kGqaPartsWaves, T, nw);
     const uint32_t used = *pool.used, np = min(used, pool.cap);
     const bool spilled = used > pool.cap;  // pieces were stored at once: no row is merged here
+    if (X0 >= X1) return;
     // the row holding list position x (0 <= x < T)
     auto locate = [&](int64_t x, int &r, int64_t &row0, int &nrow) {
         const int kvh = static_cast<int>(x / Ctot);
@@ -671,18 +679,54 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
         nrow = static_cast<int>(C[lo + 1] - C[lo]);
     };
     auto merged = [&](int64_t row0, int nrow) { return !spilled && row0 >= X0 && row0 + nrow <= X1; };
-    if (X0 >= X1) return;
+    auto lds_barrier = [] {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+    };
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t *need = pool.need;
-    int32_t &nruns = *pool.nruns;
 
-    // the pieces in tile order (their first tiles are distinct)
-    for (int b = threadIdx.x; b < static_cast<int>(np); b += NT) {
-        const int64_t k = pool.key[b];
-        int r = 0;
-        for (int b2 = 0; b2 < static_cast<int>(np); ++b2) r += pool.key[b2] < k;
-        pool.order[r] = b;
+    // tile order (unused when spilled: every piece then goes to the workspace)
+    if (!spilled)
+        for (int b = threadIdx.x; b < static_cast<int>(np); b += NT) {
+            const int w = pool.key[b] >> 16;
+            int base = 0;
+            for (int w2 = 0; w2 < w; ++w2) base += pool.count[w2];
+            pool.order[base + (pool.key[b] & 0xffff)] = b;
+        }
+    // the waves whose shares start a partition of a row that the merge pass takes
+    if (threadIdx.x < kGqaPartsWaves) {
+        const int64_t w = vw0 + threadIdx.x, xb = balanced_begin(w, T, nw);
+        bool nd = false;
+        if (xb < balanced_begin(w + 1, T, nw)) {
+            int r;
+            int64_t row0;
+            int nrow;
+            locate(xb, r, row0, nrow);
+            nd = (xb - row0) % PT == 0 && !merged(row0, nrow);
+        }
+        pool.need[threadIdx.x] = nd;
     }
+    lds_barrier();
+    // runs of pieces of one row, in order: their first places (the keys' room is free now)
+    int32_t *runs = pool.key;
+    if (wave == 0) {
+        int nr = 0;
+        for (int base = 0; base < static_cast<int>(np); base += 64) {
+            const int i = base + lane;
+            const int b = spilled ? i : pool.order[i < static_cast<int>(np) ? i : 0];
+            const int bp = spilled ? i - 1 : pool.order[i > 0 && i < static_cast<int>(np) ? i - 1 : 0];
+            const bool st = i < static_cast<int>(np) && (i == 0 || pool.row[b] != pool.row[bp]);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(st);
+            if (st) runs[nr + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = i;
+            nr += __builtin_popcountll(m);
+        }
+        if (lane == 0) {
+            runs[nr] = static_cast<int>(np);
+            *pool.nruns = nr;
+        }
+    }
+    lds_barrier();
+
     // flags of the rows that start here
     {
         int r0;
@@ -697,39 +741,9 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
             flags[r] = merged(rs, static_cast<int>(C[s + 1] - C[s])) ? 1 : 0;
         }
     }
-    // the waves whose shares start a partition of a row that the merge pass takes
-    if (threadIdx.x < kGqaPartsWaves) {
-        const int64_t w = vw0 + threadIdx.x, xb = balanced_begin(w, T, nw);
-        bool nd = false;
-        if (xb < balanced_begin(w + 1, T, nw)) {
-            int r;
-            int64_t row0;
-            int nrow;
-            locate(xb, r, row0, nrow);
-            nd = (xb - row0) % PT == 0 && !merged(row0, nrow);
-        }
-        need[threadIdx.x] = nd;
-    }
-    __syncthreads();
-    // runs of pieces of one row: their starts in tile order (the keys' room is free now)
-    int32_t *runs = reinterpret_cast<int32_t *>(pool.key);
-    if (wave == 0) {
-        int nr = 0;
-        for (int base = 0; base < static_cast<int>(np); base += 64) {
-            const int i = base + lane;
-            const bool st = i < static_cast<int>(np) && (i == 0 || pool.row[pool.order[i]] != pool.row[pool.order[i - 1]]);
-            const uint64_t m = __builtin_amdgcn_ballot_w64(st);
-            if (st) runs[nr + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = i;
-            nr += __builtin_popcountll(m);
-        }
-        if (lane == 0) {
-            runs[nr] = static_cast<int>(np);
-            nruns = nr;
-        }
-    }
     for (int c = threadIdx.x; c < kGqaPartsWaves * G * 32; c += NT) {
         const int w = c / (G * 32), cc = c - w * G * 32;
-        if (!need[w]) continue;
+        if (!pool.need[w]) continue;
         float *pa, *pm, *pl;
         piece_dest(p, -(vw0 + w + 1), cc >> 5, pa, pm, pl);
         *reinterpret_cast<f32x4 *>(pa + (cc & 31) * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -738,12 +752,13 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
             *pl = 0.f;
         }
     }
-    __syncthreads();
     // each wave takes runs in turn: a row merged here goes to the output, any other row's pieces
     // to the workspace; a lane holds 16 bytes (4 columns of one head)
+    const int nruns = *pool.nruns;
+    auto at = [&](int i) { return spilled ? i : pool.order[i]; };
     for (int k = wave; k < nruns; k += kGqaPartsWaves) {
         const int i0 = runs[k], i1 = runs[k + 1];
-        const int r = pool.row[pool.order[i0]];
+        const int r = pool.row[at(i0)];
         const int kvh = r / S, s = r - kvh * S;
         const int64_t row0 = kvh * Ctot + C[s];
         if (merged(row0, static_cast<int>(C[s + 1] - C[s]))) {
@@ -752,25 +767,45 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
                 const int hj = c >> 5;
                 float M = -INFINITY, L = 0.f;
                 f32x4 O = {0.f, 0.f, 0.f, 0.f};
-                for (int t = i0; t < i1; ++t) {
-                    const float *pc = pool.piece + static_cast<int64_t>(pool.order[t]) * G * (D + 2);
-                    const float mg = pc[G * D + hj], lg = pc[G * (D + 1) + hj];
-                    const f32x4 og = *reinterpret_cast<const f32x4 *>(pc + c * 4);
-                    const float Mn = fmaxf(M, mg);
-                    const float Mr = Mn == -INFINITY ? 0.f : Mn;
-                    const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
-                    L = fmaf(lg, f, L * a);
+                for (int t0 = i0; t0 < i1; t0 += NB) {
+                    float mg[NB], lg[NB];
+                    f32x4 og[NB];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) O[e] = fmaf(og[e], f, O[e] * a);
-                    M = Mn;
+                    for (int u = 0; u < NB; ++u) {
+                        mg[u] = -INFINITY;
+                        lg[u] = 0.f;
+                        og[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (t0 + u < i1) {
+                            const float *pc = pool.piece + static_cast<int64_t>(pool.order[t0 + u]) * G * (D + 2);
+                            mg[u] = pc[G * D + hj];
+                            lg[u] = pc[G * (D + 1) + hj];
+                            og[u] = *reinterpret_cast<const f32x4 *>(pc + c * 4);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < NB; ++u) {
+                        if (t0 + u >= i1) break;
+                        const float Mn = fmaxf(M, mg[u]);
+                        const float Mr = Mn == -INFINITY ? 0.f : Mn;
+                        const float a = fast_exp2(M - Mr), f = fast_exp2(mg[u] - Mr);
+                        L = fmaf(lg[u], f, L * a);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) O[e] = fmaf(og[u][e], f, O[e] * a);
+                        M = Mn;
+                    }
                 }
+                // four outputs, each O / L as the merge pass takes it, in one 8-byte store
+                float o[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) E::store(p.out, (row_q0 + hj) * D + (c & 31) * 4 + e, L > 0.f ? O[e] / L : 0.f);
+                for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
+                const u32x2 packed = {M::pack2(o[0], o[1]), M::pack2(o[2], o[3])};
+                *reinterpret_cast<u32x2 *>(static_cast<char *>(p.out) + ((row_q0 + hj) * D + (c & 31) * 4) * 2) =
+                    packed;
             }
         } else {
             for (int c = lane; c < (i1 - i0) * G * 32; c += 64) {
                 const int t = c / (G * 32), cc = c - t * G * 32, hj = cc >> 5;
-                const int b = pool.order[i0 + t];
+                const int b = at(i0 + t);
                 const float *pc = pool.piece + static_cast<int64_t>(b) * G * (D + 2);
                 float *pa, *pm, *pl;
                 piece_dest(p, pool.dst[b], hj, pa, pm, pl);
@@ -794,15 +829,17 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
     const int cbytes = ((p.num_seqs + 1) * 4 + 15) / 16 * 16;
     uint32_t *C = reinterpret_cast<uint32_t *>(smem + kPartsKtBytes);
     char *rest = smem + kPartsKtBytes + cbytes;
-    // the pool: a 48-byte header (counter, run count, per-wave flags), then dst [cap], key [cap],
-    // row [cap], order [cap], then the pieces
-    static_assert(kGqaPartsWaves <= 10, "the pool header holds one flag per wave");
-    const uint32_t cap = static_cast<uint32_t>((kPartsLdsBytes - kPartsKtBytes - cbytes - 80) / (G * (D + 2) * 4 + 24));
-    char *q0 = rest + 48;
-    const PiecePool pool{reinterpret_cast<float *>(q0 + (cap * 24 + 15) / 16 * 16), reinterpret_cast<int64_t *>(q0),
-                         reinterpret_cast<int64_t *>(q0 + cap * 8), reinterpret_cast<int32_t *>(q0 + cap * 16),
-                         reinterpret_cast<int32_t *>(q0 + cap * 20), reinterpret_cast<uint32_t *>(rest), cap,
-                         reinterpret_cast<int32_t *>(rest + 4), reinterpret_cast<uint32_t *>(rest + 8)};
+    // the pool: an 80-byte header (counter, run count, per-wave flags and piece counts), then
+    // dst [cap], key [cap + 1] (the runs share its room), row [cap], order [cap], then the pieces,
+    // 16-byte aligned
+    static_assert(2 * kGqaPartsWaves <= 18, "the pool header holds two words per wave");
+    const uint32_t cap = static_cast<uint32_t>((kPartsLdsBytes - kPartsKtBytes - cbytes - 112) / (G * (D + 2) * 4 + 20));
+    char *q0 = rest + 80;
+    const PiecePool pool{reinterpret_cast<float *>(q0 + (cap * 20 + 4 + 15) / 16 * 16), reinterpret_cast<int64_t *>(q0),
+                         reinterpret_cast<int32_t *>(q0 + cap * 8), reinterpret_cast<int32_t *>(q0 + cap * 12 + 4),
+                         reinterpret_cast<int32_t *>(q0 + cap * 16 + 4), reinterpret_cast<uint32_t *>(rest), cap,
+                         reinterpret_cast<int32_t *>(rest + 4), reinterpret_cast<uint32_t *>(rest + 8),
+                         reinterpret_cast<uint32_t *>(rest + 8 + 4 * kGqaPartsWaves)};
     if (threadIdx.x == 0) *pool.used = 0u;
     // the prefix scan's scratch sits where the pool will be (its last use precedes its last barrier)
     const int64_t slots = parts_slot_count(p.balanced_wgs, G);
@@ -811,7 +848,9 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nw = static_cast<int64_t>(p.balanced_wgs) * kGqaPartsWaves;
     const int64_t vw0 = balanced_virtual(blockIdx.x, p.balanced_wgs) * kGqaPartsWaves;
-    gqa_share<E, B, PAGED, POL, QL>(p, C, vw0 + wave, nw, reinterpret_cast<u32x4 *>(smem) + wave * 256, pool);
+    const int npieces =
+        gqa_share<E, B, PAGED, POL, QL>(p, C, vw0 + wave, nw, reinterpret_cast<u32x4 *>(smem) + wave * 256, pool);
+    if ((threadIdx.x & 63) == 0) pool.count[wave] = npieces;
     __syncthreads();
     parts_drain<E>(p, C, pool, vw0, nw, reinterpret_cast<int32_t *>(prefix + kBalancedMaxSeqs + 1));
 }

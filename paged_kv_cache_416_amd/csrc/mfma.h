@@ -95,6 +95,10 @@ __device__ inline u32x2 lds_read_tr16(const void *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima): before a barrier that orders LDS
+// work only, so global loads stay in flight and global stores need not complete.
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // Table entries as scalar loads: the constant address space (the tables are not written while
 // a kernel runs) with a uniform index gives s_load, whose completion counter is not the one the
 // K/V loads use, so looking an entry up never waits for K/V data.

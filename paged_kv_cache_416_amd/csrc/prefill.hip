@@ -38,9 +38,6 @@ struct PrefillParams {
     float scale_log2;
 };
 
-// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima: the global loads of later steps
-// stay in flight across the barrier)
-constexpr int kWaitLgkm0 = 0xC07F;
 
 // POS: the scale is positive, so the maximum of the scaled logits is the scale times the
 // maximum of the raw ones, and each weight's exponent is one fma of its raw logit.
