@@ -34,6 +34,9 @@ struct Mfma<F16> {
     static __device__ inline float value(unsigned short b) {
         return static_cast<float>(__builtin_bit_cast(_Float16, b));
     }
+    // the fp32 values of the low and high halves of a packed word
+    static __device__ inline float lo(unsigned w) { return value(static_cast<unsigned short>(w & 0xffffu)); }
+    static __device__ inline float hi(unsigned w) { return value(static_cast<unsigned short>(w >> 16)); }
     static __device__ inline unsigned pack2(float lo, float hi) {
         const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};  // round to nearest even
         return __builtin_bit_cast(unsigned, v);
@@ -60,6 +63,14 @@ struct Mfma<BF16> {
         return __builtin_bit_cast(unsigned short, h);
     }
     static __device__ inline float value(unsigned short b) { return __uint_as_float(static_cast<unsigned>(b) << 16); }
+    // the fp32 values of the low and high halves of a packed word: each half moved to (or left
+    // at) the top of a word, one instruction
+    static __device__ inline float lo(unsigned w) {
+        // bytes 1, 0 of w over two zero bytes (a byte permute: a shift of a packed conversion's
+        // result is otherwise rebuilt from a second conversion)
+        return __uint_as_float(__builtin_amdgcn_perm(0u, w, 0x01000c0cu));
+    }
+    static __device__ inline float hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
     static __device__ inline unsigned pack2(float lo, float hi) {
         const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};  // round to nearest even
         return __builtin_bit_cast(unsigned, v);

@@ -217,15 +217,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         // running maximum only when some row's maximum passes it by more than kMaxSlack, so the
         // rescale is rare; the weights stay below 2^kMaxSlack, and the quotient acc / l does not
         // depend on the reference.
-        float m_new[RT];
         bool grow = false;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const float mx = max_over_lane_groups(mloc[rt]);
-            m_new[rt] = fmaxf(m[rt], POS ? mx * p.scale_log2 : mx);
-            grow = grow || m_new[rt] > m[rt] + kMaxSlack;
-        }
+        for (int rt = 0; rt < RT; ++rt) grow = grow || (POS ? mloc[rt] * p.scale_log2 : mloc[rt]) > m[rt] + kMaxSlack;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            float m_new[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const float mx = max_over_lane_groups(mloc[rt]);
+                m_new[rt] = fmaxf(m[rt], POS ? mx * p.scale_log2 : mx);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const float ref = m_new[rt] == -INFINITY ? 0.f : m_new[rt];
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                     const float e1 = fast_exp2(POS ? fmaf(a1, p.scale_log2, -m_ref) : a1 - m_ref);
                     const unsigned hw = M::pack2(e0, e1);
                     h[2 * u + w] = hw;
-                    r[2 * u + w] = M::pack2(e0 - M::value(hw & 0xffffu), e1 - M::value(hw >> 16));
+                    r[2 * u + w] = M::pack2(e0 - M::lo(hw), e1 - M::hi(hw));
                 }
             const u32x4 ph = {h[0], h[1], h[2], h[3]}, pr = {r[0], r[1], r[2], r[3]};
 #pragma unroll
