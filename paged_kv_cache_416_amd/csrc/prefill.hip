@@ -155,6 +155,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // the staged step in buffer b against every row tile of the wave
     auto consume = [&](int b, int t, const bool ok[2]) {
+        // The two matrix-core sections (the logits; the weighted sums with the second tile's
+        // weights) run at raised wave priority: the other wave of the SIMD, from another
+        // workgroup, then fills the issue slots around them instead of delaying them.
+        __builtin_amdgcn_s_setprio(1);
         f32x4 c[RT][2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -181,6 +185,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 vt[j] = u32x4{a.x, a.y, c2.x, c2.y};
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // The row tiles' softmax runs phase by phase over all of them, with one branch per phase
         // at most, so the tiles' independent chains share basic blocks and interleave.
         float sc[RT][2][4], mloc[RT];
@@ -238,6 +243,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
                 m[rt] = m_new[rt];
             }
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const float m_ref = m[rt] == -INFINITY ? 0.f : m[rt];
@@ -268,6 +274,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // one step: stage the loaded rows in LDS, reuse the registers for the step two ahead, wait
