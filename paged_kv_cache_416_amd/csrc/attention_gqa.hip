@@ -623,18 +623,31 @@ __device__ inline int gqa_share(const AttnParams &p, const uint32_t *C, int64_t 
     };
 
     // A ring of two stages: while one is consumed the other is in flight.
+    // The two waves of a SIMD (w and w ^ 4) keep level: each publishes the tiles it has yet to
+    // request, and the one with more left runs at raised priority. The SIMD's issue arbitration
+    // otherwise serves the older wave first, and the younger one ends well after it. The room of
+    // the pool's per-wave flags is free until the drain.
+    const int me = static_cast<int>(v & (kGqaPartsWaves - 1));
     Stage R[2];
     issue(R[0]);
     __builtin_amdgcn_sched_barrier(0);
     for (;;) {
         if (!R[0].valid) break;
+        const uint32_t mine = static_cast<uint32_t>(xe - x);
+        pool.need[me] = mine;
+        const uint32_t other = pool.need[me ^ 4];
         issue(R[1]);
         consume(R[0]);
+        if (mine > other)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         issue(R[0]);
         consume(R[1]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     return npieces;
 }
 
@@ -841,6 +854,7 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
                          reinterpret_cast<int32_t *>(rest + 4), reinterpret_cast<uint32_t *>(rest + 8),
                          reinterpret_cast<uint32_t *>(rest + 8 + 4 * kGqaPartsWaves)};
     if (threadIdx.x == 0) *pool.used = 0u;
+    if (threadIdx.x < kGqaPartsWaves) pool.need[threadIdx.x] = 0xffffffffu;  // no progress published yet
     // the prefix scan's scratch sits where the pool will be (its last use precedes its last barrier)
     const int64_t slots = parts_slot_count(p.balanced_wgs, G);
     uint32_t *prefix = reinterpret_cast<uint32_t *>(p.ws + parts_prefix_offset(p.ws_rows, D, slots));
