@@ -404,7 +404,9 @@ struct PiecePool {
     uint32_t *used;
     uint32_t cap;
     int32_t *nruns;   // after the last wave: runs of pieces of one row
-    uint32_t *need;   // after the last wave: per wave of the workgroup, its slot is written neutral
+    uint32_t *need;   // per wave of the workgroup: while streaming, the tiles it has yet to request
+                      // (its SIMD partner levels against it); after the last wave, whether its
+                      // slot is written neutral
     uint32_t *count;  // per wave of the workgroup: its pieces
 };
 
