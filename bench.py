@@ -91,11 +91,13 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-gqa-leg", action="store_true",
-                    help="with the 13B workload, skip the 8B-shaped grouped-query leg (gqa_8b)")
+                    help="with the 13B workload, skip the 8B-shaped grouped-query legs (decode: gqa_8b; and the "
+                         "default prefill leg)")
     ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
     ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
-    ap.add_argument("--prefill", type=int, default=0, metavar="PROMPT_LEN",
-                    help="also time paged prefill of 8 prompts of this length (8B shape)")
+    ap.add_argument("--prefill", type=int, default=None, metavar="PROMPT_LEN",
+                    help="also time paged prefill of 8 prompts of this length (8B shape); 0 skips it. Default: "
+                         "2048 with the 13B workload and its grouped-query legs, else skipped")
     ap.add_argument("--memory-sim", action="store_true",
                     help="host only: run the continuous-batching memory simulator and print its JSON line")
     ap.add_argument("--cpu-one-thread", nargs=2, metavar=("WORKLOAD", "PARTITION"), help=argparse.SUPPRESS)
@@ -405,9 +407,6 @@ def main():
     if args.prefix_cache:
         result["prefix_cache"] = prefix_cache_leg()
 
-    if args.prefill:
-        result["prefill"] = prefill_leg(dev, args.prefill)
-
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.workload, P, unique_b, args.cpu_seconds)
 
@@ -415,6 +414,12 @@ def main():
         del st, cache
         torch.cuda.empty_cache()
         result["gqa_8b"] = gqa_leg(args, dev, with_cpu=not args.no_cpu_baseline)
+
+    prefill_len = args.prefill
+    if prefill_len is None:
+        prefill_len = 2048 if args.workload == "13b" and not args.no_gqa_leg else 0
+    if prefill_len:
+        result["prefill"] = prefill_leg(dev, prefill_len)
 
     print(json.dumps(result), flush=True)
 

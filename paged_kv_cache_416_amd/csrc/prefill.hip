@@ -9,8 +9,8 @@
 // wave RT tiles of 16) and walks the keys up to its last row's position in steps of 32:
 //  * the step's keys and values (16 KiB, two 16-key tiles) are read once per workgroup, whole
 //    rows per load, through the block table, and written to a double-buffered LDS ring (rows
-//    padded to 272 bytes, so the operand reads below hit 16 distinct bank groups); one barrier
-//    per step;
+//    padded to 288 bytes: each row starts eight banks after the one before, which leaves both
+//    operand reads below free of bank conflicts); one barrier per step;
 //  * logits: S^T[key][row] = K[key][:] . Q^T[:][row] as 4 v_mfma_f32_16x16x32 per 16-key tile;
 //  * weighted sum: O^T[d][row] = V^T[d][key] . P^T[key][row] as 8 v_mfma_f32_16x16x32 per
 //    16-bit part of the weights, the k slots 8g .. 8g+7 of lane group g taking keys 4g .. 4g+3 of
@@ -26,7 +26,7 @@ namespace {
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowTiles = 2;  // 16-row tiles per wave
 constexpr int kStepKeys = 32;        // keys per step (two 16-key tiles)
-constexpr int kLdsRow = 272;         // bytes per staged row: 256 + 16 of padding
+constexpr int kLdsRow = 288;         // bytes per staged row: 256 + 32 of padding
 constexpr float kMaxSlack = 8.f;     // log2 units the softmax reference may lag the running maximum
 
 struct PrefillParams {
