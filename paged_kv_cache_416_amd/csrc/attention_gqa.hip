@@ -872,15 +872,18 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
 }
 
 // The merge pass of the persistent schedule, for the rows the attention kernel left to it (its
-// flags): grid = (num_kv_heads, num_seqs), 256 threads over
-// the group's G heads x 128 columns, one pass with a running maximum over the row's partitions
-// (their workspace rows), then over the slots of the waves whose shares begin inside the row
-// (owner of its first tile < w <= owner of its last: a cut piece of one of its partitions, or
-// neutral). The share boundaries depend only on the tile count.
+// flags): grid = (num_kv_heads, num_seqs), one lane per 4 adjacent columns of the group's G heads
+// (G x 32 lanes), one pass with a running maximum over the row's partitions (their workspace
+// rows), then over the slots of the waves whose shares begin inside the row (owner of its first
+// tile < w <= owner of its last: a cut piece of one of its partitions, or neutral). The share
+// boundaries depend only on the tile count. The work is a chain of dependent loads (the flags,
+// then the pieces), so the lanes take all their columns in one pass, with 16-byte loads and 16
+// pieces in flight at a time.
 template <class E>
-__global__ __launch_bounds__(256) void attn_gqa_reduce_parts_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kGqaMaxGroup * 32) void attn_gqa_reduce_parts_kernel(const AttnParams p) {
     constexpr int D = 128;
     constexpr int TR = 16;
+    constexpr int NB = 16;
     const int kvh = blockIdx.x, s = blockIdx.y, G = p.group;
     const int64_t nsl = parts_slot_count(p.balanced_wgs, G);
     const float *sl = p.ws + parts_slot_offset(p.ws_rows, D);
@@ -893,51 +896,54 @@ __global__ __launch_bounds__(256) void attn_gqa_reduce_parts_kernel(const AttnPa
     const int PT = p.partition_size / TR;
     const int64_t row0 = kvh * Ctot + c0;
     const int nrow = static_cast<int>(c1 - c0);
-    if (nrow > 0 && done) return;  // merged by the attention kernel
+    const int c = threadIdx.x;
+    if ((nrow > 0 && done) || c >= G * 32) return;  // merged by the attention kernel; a lane past the group
     const int np = (nrow + PT - 1) / PT;
     const int64_t w0 = nrow > 0 ? balanced_owner(row0, T, nw) + 1 : 0;
     const int64_t w1 = nrow > 0 ? balanced_owner(row0 + nrow - 1, T, nw) : -1;
     const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
-    for (int i = threadIdx.x; i < G * D; i += 256) {
-        const int j = i / D, d = i % D;
-        float M = -INFINITY, L = 0.f, O = 0.f;
-        auto add = [&](float mg, float lg, float og) {
-            const float Mn = fmaxf(M, mg);
-            const float Mr = Mn == -INFINITY ? 0.f : Mn;
-            const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
-            L = fmaf(lg, f, L * a);
-            O = fmaf(og, f, O * a);
-            M = Mn;
-        };
-        const int64_t wr = (row_q0 + j) * p.num_parts;
-        const int total = np + static_cast<int>(w1 - w0 + 1);
-        // both kinds of piece in batches of 8: a batch's loads are issued together, then merged
-        // in order (a loop that runs its last iterations one by one waits a load latency for each)
-        constexpr int NB = 8;
-        for (int t0 = 0; t0 < total; t0 += NB) {
-            float mg[NB], lg[NB], og[NB];
+    const int j = c >> 5, d4 = (c & 31) * 4;
+    float M = -INFINITY, L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    const int64_t wr = (row_q0 + j) * p.num_parts;
+    const int total = np + static_cast<int>(w1 - w0 + 1);
+    for (int t0 = 0; t0 < total; t0 += NB) {
+        float mg[NB], lg[NB];
+        f32x4 og[NB];
 #pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const int t = t0 + u;
-                mg[u] = -INFINITY;
-                lg[u] = 0.f;
-                og[u] = 0.f;
-                if (t < total) {
-                    const bool row = t < np;
-                    const int64_t r = row ? wr + t : (w0 + t - np) * G + j;
-                    const float *base = row ? p.ws : sl;
-                    const int64_t rows = row ? p.ws_rows : nsl;
-                    mg[u] = base[rows * D + r];
-                    lg[u] = base[rows * (D + 1) + r];
-                    og[u] = base[r * D + d];
-                }
+        for (int u = 0; u < NB; ++u) {
+            const int t = t0 + u;
+            mg[u] = -INFINITY;
+            lg[u] = 0.f;
+            og[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < total) {
+                const bool row = t < np;
+                const int64_t r = row ? wr + t : (w0 + t - np) * G + j;
+                const float *base = row ? p.ws : sl;
+                const int64_t rows = row ? p.ws_rows : nsl;
+                mg[u] = base[rows * D + r];
+                lg[u] = base[rows * (D + 1) + r];
+                og[u] = *reinterpret_cast<const f32x4 *>(base + r * D + d4);
             }
-#pragma unroll
-            for (int u = 0; u < NB; ++u)
-                if (t0 + u < total) add(mg[u], lg[u], og[u]);
         }
-        E::store(p.out, (row_q0 + j) * D + d, L > 0.f ? O / L : 0.f);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (t0 + u < total) {  // a guard, not a break: the loop unrolls and the pieces stay in registers
+                const float Mn = fmaxf(M, mg[u]);
+                const float Mr = Mn == -INFINITY ? 0.f : Mn;
+                const float a = fast_exp2(M - Mr), f = fast_exp2(mg[u] - Mr);
+                L = fmaf(lg[u], f, L * a);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[e] = fmaf(og[u][e], f, O[e] * a);
+                M = Mn;
+            }
+        }
     }
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
+    const u32x2 packed = {Mfma<E>::pack2(o[0], o[1]), Mfma<E>::pack2(o[2], o[3])};
+    *reinterpret_cast<u32x2 *>(static_cast<char *>(p.out) + ((row_q0 + j) * D + d4) * 2) = packed;
 }
 
 template <class E, int B, bool PAGED, int POL>
@@ -979,8 +985,8 @@ int launch_one(const AttnParams &p, int32_t num_seqs, int32_t grid_parts, hipStr
                                    0, stream, q);
             int rc = hip_status(hipGetLastError(), "grouped-query attention launch");
             if (rc) return rc;
-            hipLaunchKernelGGL((attn_gqa_reduce_parts_kernel<E>), dim3(p.num_kv_heads, num_seqs), dim3(256), 0, stream,
-                               q);
+            hipLaunchKernelGGL((attn_gqa_reduce_parts_kernel<E>), dim3(p.num_kv_heads, num_seqs),
+                               dim3((q.group * 32 + 63) / 64 * 64), 0, stream, q);
             return hip_status(hipGetLastError(), "grouped-query reduce launch");
         }
     }
