@@ -408,12 +408,25 @@ struct PiecePool {
                       // (its SIMD partner levels against it); after the last wave, whether its
                       // slot is written neutral
     uint32_t *count;  // per wave of the workgroup: its pieces
+    int32_t *first_row;  // the first work row that starts in the workgroup's tiles (from wave 0's
+                         // share), or -1 when wave 0's share is empty
+};
+
+// Where a wave's share starts: the row holding its first tile (none for an empty share), and
+// whether that tile starts one of the row's partitions.
+struct ShareHead {
+    bool has = false;
+    bool starts_row = false;
+    bool starts_part = false;
+    int r = 0;         // work row: kv head * num_seqs + sequence
+    int nrow = 0;      // the row's tiles
+    int64_t row0 = 0;  // its first tile's list position
 };
 
 // Returns the number of pieces the wave finished (uniform).
 template <class E, int B, bool PAGED, int POL, int QL>
 __device__ inline int gqa_share(const AttnParams &p, const uint32_t *C, int64_t v, int64_t nw, u32x4 *kt,
-                                const PiecePool &pool) {
+                                const PiecePool &pool, ShareHead &head) {
     constexpr int D = 128;
     constexpr int TR = 16;
     constexpr int SPB = B / TR;
@@ -475,6 +488,12 @@ __device__ inline int gqa_share(const AttnParams &p, const uint32_t *C, int64_t 
     };
     locate();
     lookup();
+    head.has = true;
+    head.starts_row = x == row0;
+    head.starts_part = x == pbeg;
+    head.r = kvh * S_ + s;
+    head.nrow = nrow;
+    head.row0 = row0;
 
     struct Stage {
         u32x4 k[4], v[4];  // [i]: chunk n of row 4g + i
@@ -668,13 +687,12 @@ constexpr int kPartsKtBytes = kGqaPartsWaves * 16 * 16 * 16;
 // write comes after the last barrier (a block barrier would also wait for stores to complete).
 template <class E>
 __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const PiecePool &pool, int64_t vw0,
-                                   int64_t nw, int32_t *flags) {
+                                   int64_t nw, int32_t *flags, const ShareHead &head) {
     using M = Mfma<E>;
     constexpr int D = 128;
-    constexpr int TR = 16;
     constexpr int NT = kGqaPartsWaves * 64;
     constexpr int NB = 8;  // pieces whose loads are in flight together while a row is merged
-    const int G = p.group, S = p.num_seqs, PT = p.partition_size / TR;
+    const int G = p.group, S = p.num_seqs;
     const int64_t Ctot = C[S], T = Ctot * p.num_kv_heads;
     const int64_t X0 = balanced_begin(vw0, T, nw), X1 = balanced_begin(vw0 + kGqaPartsWaves, T, nw);
     const uint32_t used = *pool.used, np = min(used, pool.cap);
@@ -708,21 +726,13 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
             for (int w2 = 0; w2 < w; ++w2) base += pool.count[w2];
             pool.order[base + (pool.key[b] & 0xffff)] = b;
         }
-    // the waves whose shares start a partition of a row that the merge pass takes
-    if (threadIdx.x < kGqaPartsWaves) {
-        const int64_t w = vw0 + threadIdx.x, xb = balanced_begin(w, T, nw);
-        bool nd = false;
-        if (xb < balanced_begin(w + 1, T, nw)) {
-            int r;
-            int64_t row0;
-            int nrow;
-            locate(xb, r, row0, nrow);
-            nd = (xb - row0) % PT == 0 && !merged(row0, nrow);
-        }
-        pool.need[threadIdx.x] = nd;
-    }
+    // the waves whose shares start a partition of a row that the merge pass takes (each wave's own
+    // share start, as its stream found it)
+    if (lane == 0) pool.need[wave] = head.has && head.starts_part && !merged(head.row0, head.nrow);
     lds_barrier();
-    // runs of pieces of one row, in order: their first places (the keys' room is free now)
+    // runs of pieces of one row, in order: their first places (the keys' room is free now), each
+    // tagged kRunMerged when its row is merged here
+    constexpr int kRunMerged = 1 << 30;
     int32_t *runs = pool.key;
     if (wave == 0) {
         int nr = 0;
@@ -732,7 +742,11 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
             const int bp = spilled ? i - 1 : pool.order[i > 0 && i < static_cast<int>(np) ? i - 1 : 0];
             const bool st = i < static_cast<int>(np) && (i == 0 || pool.row[b] != pool.row[bp]);
             const uint64_t m = __builtin_amdgcn_ballot_w64(st);
-            if (st) runs[nr + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = i;
+            if (st) {
+                const int r = pool.row[b], kvh = r / S, s = r - kvh * S;
+                const bool mg = merged(kvh * Ctot + C[s], static_cast<int>(C[s + 1] - C[s]));
+                runs[nr + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = i | (mg ? kRunMerged : 0);
+            }
             nr += __builtin_popcountll(m);
         }
         if (lane == 0) {
@@ -744,11 +758,13 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
 
     // flags of the rows that start here
     {
-        int r0;
-        int64_t row0;
-        int nrow;
-        locate(X0, r0, row0, nrow);
-        if (row0 < X0) ++r0;  // the row holding X0 starts in an earlier workgroup
+        int r0 = *pool.first_row;
+        if (r0 < 0) {  // wave 0's share is empty: the row holding X0, unless it starts earlier
+            int64_t row0;
+            int nrow;
+            locate(X0, r0, row0, nrow);
+            if (row0 < X0) ++r0;
+        }
         for (int r = r0 + threadIdx.x; r < p.num_kv_heads * S; r += NT) {
             const int kvh = r / S, s = r - kvh * S;
             const int64_t rs = kvh * Ctot + C[s];
@@ -767,67 +783,115 @@ __device__ inline void parts_drain(const AttnParams &p, const uint32_t *C, const
             *pl = 0.f;
         }
     }
-    // each wave takes runs in turn: a row merged here goes to the output, any other row's pieces
-    // to the workspace; a lane holds 16 bytes (4 columns of one head)
+    // A row merged here goes to the output, the rows one per wave in turn (a row's merge is one
+    // chain over its pieces). Any other row's pieces go to the workspace, shared out over all the
+    // waves, a piece per wave in turn: copied by one wave, a cut row of tens of pieces held up the
+    // workgroup's end by microseconds. A lane holds 16 bytes (4 columns of one head). The runs'
+    // entries are read 63 at a time, one a lane.
     const int nruns = *pool.nruns;
     auto at = [&](int i) { return spilled ? i : pool.order[i]; };
-    for (int k = wave; k < nruns; k += kGqaPartsWaves) {
-        const int i0 = runs[k], i1 = runs[k + 1];
-        const int r = pool.row[at(i0)];
-        const int kvh = r / S, s = r - kvh * S;
-        const int64_t row0 = kvh * Ctot + C[s];
-        if (merged(row0, static_cast<int>(C[s + 1] - C[s]))) {
-            const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
-            for (int c = lane; c < G * 32; c += 64) {
-                const int hj = c >> 5;
-                float M = -INFINITY, L = 0.f;
-                f32x4 O = {0.f, 0.f, 0.f, 0.f};
-                for (int t0 = i0; t0 < i1; t0 += NB) {
-                    float mg[NB], lg[NB];
-                    f32x4 og[NB];
+    for (int kb = 0; kb < nruns; kb += 63) {
+        const int ent = runs[min(kb + lane, nruns)];
+        const int kn = min(63, nruns - kb);
+        for (int kk = 0; kk < kn; ++kk) {
+            const int e0 = __builtin_amdgcn_readlane(ent, kk), e1 = __builtin_amdgcn_readlane(ent, kk + 1);
+            const int i0 = e0 & ~kRunMerged, i1 = e1 & ~kRunMerged;
+            if (e0 & kRunMerged) {
+                if ((kb + kk) % kGqaPartsWaves != wave) continue;
+                const int r = pool.row[at(i0)];
+                const int kvh = r / S, s = r - kvh * S;
+                const int64_t row_q0 = static_cast<int64_t>(s) * p.num_q_heads + static_cast<int64_t>(kvh) * G;
+                // two column chunks a lane (c0 and c0 + 64) in one pass: their pieces' places are read
+                // once, and both chains of loads are in flight together
+                auto add = [](float &M, float &L, f32x4 &O, float mg, float lg, const f32x4 &og) {
+                    const float Mn = fmaxf(M, mg);
+                    const float Mr = Mn == -INFINITY ? 0.f : Mn;
+                    const float a = fast_exp2(M - Mr), f = fast_exp2(mg - Mr);
+                    L = fmaf(lg, f, L * a);
 #pragma unroll
-                    for (int u = 0; u < NB; ++u) {
-                        mg[u] = -INFINITY;
-                        lg[u] = 0.f;
-                        og[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (t0 + u < i1) {
-                            const float *pc = pool.piece + static_cast<int64_t>(pool.order[t0 + u]) * G * (D + 2);
-                            mg[u] = pc[G * D + hj];
-                            lg[u] = pc[G * (D + 1) + hj];
-                            og[u] = *reinterpret_cast<const f32x4 *>(pc + c * 4);
+                    for (int e = 0; e < 4; ++e) O[e] = fmaf(og[e], f, O[e] * a);
+                    M = Mn;
+                };
+                // four outputs, each O / L as the merge pass takes it, in one 8-byte store
+                auto put = [&](int c, float L, const f32x4 &O) {
+                    float o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
+                    const u32x2 packed = {M::pack2(o[0], o[1]), M::pack2(o[2], o[3])};
+                    const int64_t at_out = ((row_q0 + (c >> 5)) * D + (c & 31) * 4) * 2;
+                    *reinterpret_cast<u32x2 *>(static_cast<char *>(p.out) + at_out) = packed;
+                };
+                for (int c0 = lane; c0 < G * 32; c0 += 128) {
+                    const int c1 = c0 + 64;
+                    const bool has1 = c1 < G * 32;
+                    const int h0 = c0 >> 5, h1 = has1 ? c1 >> 5 : h0;
+                    float M0 = -INFINITY, L0 = 0.f, M1 = -INFINITY, L1 = 0.f;
+                    f32x4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
+                    for (int t0 = i0; t0 < i1; t0 += NB) {
+                        int bb[NB];
+#pragma unroll
+                        for (int u = 0; u < NB; ++u) bb[u] = pool.order[min(t0 + u, i1 - 1)];
+                        float mg0[NB], lg0[NB], mg1[NB], lg1[NB];
+                        f32x4 og0[NB], og1[NB];
+#pragma unroll
+                        for (int u = 0; u < NB; ++u) {
+                            const float *pc = pool.piece + static_cast<int64_t>(bb[u]) * G * (D + 2);
+                            mg0[u] = pc[G * D + h0];
+                            lg0[u] = pc[G * (D + 1) + h0];
+                            og0[u] = *reinterpret_cast<const f32x4 *>(pc + c0 * 4);
+                            mg1[u] = pc[G * D + h1];
+                            lg1[u] = pc[G * (D + 1) + h1];
+                            og1[u] = *reinterpret_cast<const f32x4 *>(pc + (has1 ? c1 : c0) * 4);
+                        }
+#pragma unroll
+                        for (int u = 0; u < NB; ++u) {
+                            if (t0 + u < i1) {
+                                add(M0, L0, O0, mg0[u], lg0[u], og0[u]);
+                                add(M1, L1, O1, mg1[u], lg1[u], og1[u]);
+                            }
                         }
                     }
-#pragma unroll
-                    for (int u = 0; u < NB; ++u) {
-                        if (t0 + u >= i1) break;
-                        const float Mn = fmaxf(M, mg[u]);
-                        const float Mr = Mn == -INFINITY ? 0.f : Mn;
-                        const float a = fast_exp2(M - Mr), f = fast_exp2(mg[u] - Mr);
-                        L = fmaf(lg[u], f, L * a);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) O[e] = fmaf(og[u][e], f, O[e] * a);
-                        M = Mn;
-                    }
+                    put(c0, L0, O0);
+                    if (has1) put(c1, L1, O1);
                 }
-                // four outputs, each O / L as the merge pass takes it, in one 8-byte store
-                float o[4];
+            } else {
+                // copied four pieces at a time, so that their LDS reads are in flight together (one
+                // chunk after another, each a chain of lookups, reads and a store, took microseconds
+                // for the rows of tens of pieces)
+                constexpr int NC = 4;
+                // this wave's pieces: i0 + wave + kGqaPartsWaves t, t < n
+                const int n = (i1 - i0 - wave + kGqaPartsWaves - 1) / kGqaPartsWaves;
+                for (int t0 = 0; t0 < n; t0 += NC) {
+                    int b[NC];
+                    int64_t code[NC];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = L > 0.f ? O[e] / L : 0.f;
-                const u32x2 packed = {M::pack2(o[0], o[1]), M::pack2(o[2], o[3])};
-                *reinterpret_cast<u32x2 *>(static_cast<char *>(p.out) + ((row_q0 + hj) * D + (c & 31) * 4) * 2) =
-                    packed;
-            }
-        } else {
-            for (int c = lane; c < (i1 - i0) * G * 32; c += 64) {
-                const int t = c / (G * 32), cc = c - t * G * 32, hj = cc >> 5;
-                const int b = at(i0 + t);
-                const float *pc = pool.piece + static_cast<int64_t>(b) * G * (D + 2);
-                float *pa, *pm, *pl;
-                piece_dest(p, pool.dst[b], hj, pa, pm, pl);
-                *reinterpret_cast<f32x4 *>(pa + (cc & 31) * 4) = *reinterpret_cast<const f32x4 *>(pc + cc * 4);
-                if ((cc & 31) == 0) {
-                    *pm = pc[G * D + hj];
-                    *pl = pc[G * (D + 1) + hj];
+                    for (int u = 0; u < NC; ++u) b[u] = at(i0 + wave + kGqaPartsWaves * min(t0 + u, n - 1));
+#pragma unroll
+                    for (int u = 0; u < NC; ++u) code[u] = pool.dst[b[u]];
+                    for (int cc = lane; cc < G * 32; cc += 64) {
+                        const int hj = cc >> 5;
+                        f32x4 o[NC];
+                        float mv[NC], lv[NC];
+#pragma unroll
+                        for (int u = 0; u < NC; ++u) {
+                            const float *pc = pool.piece + static_cast<int64_t>(b[u]) * G * (D + 2);
+                            o[u] = *reinterpret_cast<const f32x4 *>(pc + cc * 4);
+                            mv[u] = pc[G * D + hj];
+                            lv[u] = pc[G * (D + 1) + hj];
+                        }
+#pragma unroll
+                        for (int u = 0; u < NC; ++u) {
+                            if (t0 + u < n) {
+                                float *pa, *pm, *pl;
+                                piece_dest(p, code[u], hj, pa, pm, pl);
+                                *reinterpret_cast<f32x4 *>(pa + (cc & 31) * 4) = o[u];
+                                if ((cc & 31) == 0) {
+                                    *pm = mv[u];
+                                    *pl = lv[u];
+                                }
+                            }
+                        }
+                    }
                 }
             }
         }
@@ -844,17 +908,19 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
     const int cbytes = ((p.num_seqs + 1) * 4 + 15) / 16 * 16;
     uint32_t *C = reinterpret_cast<uint32_t *>(smem + kPartsKtBytes);
     char *rest = smem + kPartsKtBytes + cbytes;
-    // the pool: an 80-byte header (counter, run count, per-wave flags and piece counts), then
+    // the pool: an 80-byte header (counter, run count, per-wave flags and piece counts, the first
+    // row), then
     // dst [cap], key [cap + 1] (the runs share its room), row [cap], order [cap], then the pieces,
     // 16-byte aligned
-    static_assert(2 * kGqaPartsWaves <= 18, "the pool header holds two words per wave");
+    static_assert(2 + 2 * kGqaPartsWaves + 1 <= 20, "the pool header: two counters, two words a wave, the first row");
     const uint32_t cap = static_cast<uint32_t>((kPartsLdsBytes - kPartsKtBytes - cbytes - 112) / (G * (D + 2) * 4 + 20));
     char *q0 = rest + 80;
     const PiecePool pool{reinterpret_cast<float *>(q0 + (cap * 20 + 4 + 15) / 16 * 16), reinterpret_cast<int64_t *>(q0),
                          reinterpret_cast<int32_t *>(q0 + cap * 8), reinterpret_cast<int32_t *>(q0 + cap * 12 + 4),
                          reinterpret_cast<int32_t *>(q0 + cap * 16 + 4), reinterpret_cast<uint32_t *>(rest), cap,
                          reinterpret_cast<int32_t *>(rest + 4), reinterpret_cast<uint32_t *>(rest + 8),
-                         reinterpret_cast<uint32_t *>(rest + 8 + 4 * kGqaPartsWaves)};
+                         reinterpret_cast<uint32_t *>(rest + 8 + 4 * kGqaPartsWaves),
+                         reinterpret_cast<int32_t *>(rest + 8 + 8 * kGqaPartsWaves)};
     if (threadIdx.x == 0) *pool.used = 0u;
     if (threadIdx.x < kGqaPartsWaves) pool.need[threadIdx.x] = 0xffffffffu;  // no progress published yet
     // the prefix scan's scratch sits where the pool will be (its last use precedes its last barrier)
@@ -864,11 +930,15 @@ __global__ __launch_bounds__(kGqaPartsWaves * 64) __attribute__((amdgpu_waves_pe
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nw = static_cast<int64_t>(p.balanced_wgs) * kGqaPartsWaves;
     const int64_t vw0 = balanced_virtual(blockIdx.x, p.balanced_wgs) * kGqaPartsWaves;
-    const int npieces =
-        gqa_share<E, B, PAGED, POL, QL>(p, C, vw0 + wave, nw, reinterpret_cast<u32x4 *>(smem) + wave * 256, pool);
-    if ((threadIdx.x & 63) == 0) pool.count[wave] = npieces;
+    ShareHead head;
+    const int npieces = gqa_share<E, B, PAGED, POL, QL>(p, C, vw0 + wave, nw,
+                                                        reinterpret_cast<u32x4 *>(smem) + wave * 256, pool, head);
+    if ((threadIdx.x & 63) == 0) {
+        pool.count[wave] = npieces;
+        if (wave == 0) *pool.first_row = head.has ? head.r + (head.starts_row ? 0 : 1) : -1;
+    }
     __syncthreads();
-    parts_drain<E>(p, C, pool, vw0, nw, reinterpret_cast<int32_t *>(prefix + kBalancedMaxSeqs + 1));
+    parts_drain<E>(p, C, pool, vw0, nw, reinterpret_cast<int32_t *>(prefix + kBalancedMaxSeqs + 1), head);
 }
 
 // The merge pass of the persistent schedule, for the rows the attention kernel left to it (its
