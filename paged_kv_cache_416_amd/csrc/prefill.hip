@@ -312,17 +312,21 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2))) voi
         step(R[1], 1);
     }
 
-    // lane (n, g) holds row n's weight sum and d = 16 j + 4g + i of its output
+    // lane (n, g) holds row n's weight sum and d = 16 j + 4g + i of its output: four adjacent
+    // outputs per j, rounded to nearest even and stored as one 8-byte word
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float l = lsum[rt][0];
         if (row_ok[rt]) {
             const float inv = l > 0.f ? 1.f / l : 0.f;
-            const int64_t base = (static_cast<int64_t>(q0 + tok[rt]) * p.num_q_heads + head[rt]) * D;
+            char *base = static_cast<char *>(p.out) +
+                         (static_cast<int64_t>(q0 + tok[rt]) * p.num_q_heads + head[rt]) * D * 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) E::store(p.out, base + 16 * j + 4 * g + i, acc[rt][j][i] * inv);
+            for (int j = 0; j < 8; ++j) {
+                const f32x4 a = acc[rt][j];
+                *reinterpret_cast<u32x2 *>(base + (16 * j + 4 * g) * 2) =
+                    u32x2{M::pack2(a[0] * inv, a[1] * inv), M::pack2(a[2] * inv, a[3] * inv)};
+            }
         }
     }
 }
