@@ -331,6 +331,24 @@ def test_long_context_spans_table_chunks(dtype, hq, hkv, B):
         assert_close(gpu_attention(c, w, partition_size=P), ref, dtype, f"long P={P}")
 
 
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 2, 2), ("bf16", 8, 2)])
+def test_maximum_context(dtype, hq, hkv):
+    """A 131,072-token sequence beside a 3,000-token and a 1-token one: 8,192 table entries (128
+    refills of a wave's 64-entry table register on the one-head kernel), 256 partitions of 512
+    on the per-item grid and the persistent schedule, and one share's tiles spread over many
+    rows in the balanced split; one-head (f16) and matrix-core (bf16) kernels against the oracle
+    in every mode."""
+    w = synth.decode_workload("max", 41, [131072, 3000, 1], hq, hkv, 128, 16, dtype, 0.5, 0.5)
+    say(f"[max context {dtype} Hq={hq} Hkv={hkv}] blocks={w.num_blocks}")
+    st = oracle.replay(w)
+    ref = oracle.attention_of(st, w)
+    c = gpu_replay(w)
+    for P in (0, 512, BALANCED):
+        say(f"  [max context {dtype}] partition_size={P}")
+        err = assert_close(gpu_attention(c, w, partition_size=P), ref, dtype, f"max context P={P}")
+        say(f"  [max context {dtype}] P={P} max abs err {err:.3e}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 2, 2, 64), ("bf16", 8, 2, 128)])
 def test_balanced_at_the_sequence_limit(dtype, hq, hkv, d):
     """The balanced split at its largest batch (4096 sequences, many of them empty or shorter
