@@ -120,3 +120,45 @@ def test_prefill_full_size_sampled():
                                np.arange(len(sample) + 1, dtype=np.int32), scale, "bf16")
     assert_close(out[torch.from_numpy(rows).to(dev)], ref, "bf16", "prefill full size, sampled rows")
     assert not torch.isnan(out).any().item()
+
+
+def test_prefill_long_prompts():
+    """Long prompts in one launch: a fresh 32,768-token prompt, and the last 16,384 tokens of a
+    65,536-token context as a chunk (groups of 4 query heads, bf16, 16-token blocks in a random
+    order, 1,024 row blocks and steps of up to 2,048 keys per workgroup); sampled rows against the
+    oracle, each as one query at its position over the context truncated there, at tile and step
+    edges, the chunk's first rows and random positions."""
+    hq, hkv, d, B = 8, 2, 128, 16
+    ctxs, nq = [32768, 65536], [32768, 16384]
+    rng = np.random.default_rng(65536)
+    nbs = [c // B for c in ctxs]
+    N = sum(nbs) + 16
+    perm = rng.permutation(N).astype(np.int32)
+    tables = np.full((2, max(nbs)), -1, np.int32)
+    tables[0, :nbs[0]] = perm[:nbs[0]]
+    tables[1, :nbs[1]] = perm[nbs[0]:nbs[0] + nbs[1]]
+    k = synth.normal(rng, (N, hkv, B, d), 0.5, "bf16")
+    v = synth.normal(rng, (N, hkv, B, d), 0.5, "bf16")
+    qs = np.array([0, nq[0], nq[0] + nq[1]], np.int32)
+    q = synth.normal(rng, (int(qs[-1]), hq, d), 0.5, "bf16")
+    scale = float(np.float32(d ** -0.5))
+    from paged_kv_cache_416_amd.cache import to_device
+    dev = torch.device("cuda:0")
+    kd, vd, qd = (to_device(x, torch.bfloat16, dev) for x in (k, v, q))
+    out = torch.full_like(qd, float("nan"))
+    ctx = torch.tensor(ctxs, dtype=torch.int32, device=dev)
+    say(f"[prefill long] contexts {ctxs}, queries {nq}, {hq}/{hkv} heads")
+    kernels.paged_attention_prefill(out, qd, kd, vd, torch.from_numpy(tables).to(dev), ctx,
+                                    torch.from_numpy(qs).to(dev), max(nq), max(ctxs), scale)
+    torch.cuda.synchronize()
+    sample = []
+    for s in range(2):
+        n = nq[s]
+        idx = {0, 1, 15, 16, 31, 32, 33, 127, 128, 2047, 2048, n // 2, n - 2, n - 1, *rng.integers(0, n, 6).tolist()}
+        sample += [(s, i) for i in sorted(idx)]
+    rows = np.array([qs[s] + i for s, i in sample])
+    pos = np.array([ctxs[s] - nq[s] + i for s, i in sample], np.int32)
+    ref = oracle.paged_prefill(q[rows], k, v, tables[[s for s, _ in sample]], pos + 1,
+                               np.arange(len(sample) + 1, dtype=np.int32), scale, "bf16")
+    assert_close(out[torch.from_numpy(rows).to(dev)], ref, "bf16", "prefill long prompts, sampled rows")
+    assert not torch.isnan(out).any().item()
