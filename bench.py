@@ -94,6 +94,8 @@ def parse():
                     help="with the 13B workload, skip the 8B-shaped grouped-query legs (decode: gqa_8b; and the "
                          "default prefill leg)")
     ap.add_argument("--swap", action="store_true", help="also time preemption by swap (device <-> pinned host)")
+    ap.add_argument("--no-cache-ops-leg", action="store_true",
+                    help="with the 13B workload, skip the cache-write legs (copy_blocks, reshape_and_cache)")
     ap.add_argument("--prefix-cache", action="store_true", help="also time the host prefix cache")
     ap.add_argument("--prefill", type=int, default=None, metavar="PROMPT_LEN",
                     help="also time paged prefill of 8 prompts of this length (8B shape); 0 skips it. Default: "
@@ -415,6 +417,9 @@ def main():
         torch.cuda.empty_cache()
         result["gqa_8b"] = gqa_leg(args, dev, with_cpu=not args.no_cpu_baseline)
 
+    if args.workload == "13b" and not args.no_cache_ops_leg:
+        result["cache_ops"] = cache_ops_leg(dev)
+
     prefill_len = args.prefill
     if prefill_len is None:
         prefill_len = 2048 if args.workload == "13b" and not args.no_gqa_leg else 0
@@ -630,6 +635,47 @@ def prefill_leg(dev, prompt_len, seqs=8, hq=32, hkv=8, d=128, B=16, reps=30, war
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
                          "frac": round(tf / 2500.0, 4), "traffic": None},
             "tokens_per_s": round(seqs * prompt_len / (us * 1e-6), 0)}
+
+
+def cache_ops_leg(dev, heads=40, d=128, B=16, pairs=2048, tokens=16384, reps=50):
+    """The cache writes at the 13B shape (fp16, 40 kv heads x 128), at sizes where HBM bounds them:
+    copy_blocks of `pairs` copy-on-write pairs (distinct random sources and destinations in an
+    8192-block pool) and reshape_and_cache of a `tokens`-token chunk into its sequence's blocks
+    (random block order, consecutive slots within a block, as a prefill writes them). Algorithmic
+    bytes: every block or row read once and written once, K and V."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_416_amd import kernels
+    rng = np.random.default_rng(77)
+    N = 8192
+    k = torch.zeros(N, heads, B, d, dtype=torch.float16, device=dev)
+    v = torch.zeros_like(k)
+    block_bytes = heads * B * d * 2
+    stream = torch.cuda.current_stream()
+    perm = rng.permutation(N).astype(np.int32)
+    pair = np.stack([perm[:pairs], perm[pairs:2 * pairs]], axis=1)
+    for _ in range(5):
+        kernels.copy_blocks([k], [v], pair)
+    cb_us = timed_launches(lambda i: kernels.copy_blocks([k], [v], pair), reps, stream)
+    cb_bytes = 2 * 2 * pairs * block_bytes
+    nblk = tokens // B
+    table = rng.permutation(N)[:nblk].astype(np.int64)
+    slots = torch.from_numpy(np.repeat(table * B, B) + np.tile(np.arange(B), nblk)).to(dev)
+    key = (torch.randn(tokens, heads, d, device=dev) * 0.5).to(torch.float16)
+    val = (torch.randn(tokens, heads, d, device=dev) * 0.5).to(torch.float16)
+    for _ in range(5):
+        kernels.reshape_and_cache(key, val, k, v, slots)
+    rc_us = timed_launches(lambda i: kernels.reshape_and_cache(key, val, k, v, slots), reps, stream)
+    rc_bytes = 2 * 2 * tokens * heads * d * 2 + tokens * 8
+
+    def entry(us, nbytes, what):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"what": what, "us": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+    return {"copy_blocks": entry(cb_us, cb_bytes, f"{pairs} block pairs, K and V, 13B shape"),
+            "reshape_and_cache": entry(rc_us, rc_bytes, f"{tokens} tokens into their blocks, 13B shape")}
 
 
 def read_probe_leg(nbytes, args, dev):

@@ -12,38 +12,56 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-// One thread per 16-byte chunk of one (token, kv head) row, grid-stride.
-// Token i, head h goes to block slot/B, row slot%B of head h (slide 11: a new
-// token goes into the free slot of the sequence's last block).
+// Each thread takes kWriteUnroll 16-byte chunks of (token, kv head) rows, one grid stride apart
+// (consecutive lanes read consecutive chunks), with every load issued before the first store;
+// chunk indices below 2^31 take 32-bit arithmetic. Token i, head h goes to block slot/B, row
+// slot%B of head h (slide 11: a new token goes into the free slot of the sequence's last block).
+constexpr int kWriteUnroll = 4;
+
+template <typename I>
 __global__ __launch_bounds__(kThreads) void reshape_and_cache_kernel(
     const char *__restrict__ key, const char *__restrict__ value, int64_t key_stride_b, int64_t value_stride_b,
     char *__restrict__ k_cache, char *__restrict__ v_cache, int64_t num_slots, const int64_t *__restrict__ slots,
     int64_t total_chunks, int32_t chunks_per_row, int32_t num_kv_heads, int32_t block_size, int32_t block_shift) {
     const int32_t row_bytes = chunks_per_row * 16;
-    const int64_t per_token = static_cast<int64_t>(chunks_per_row) * num_kv_heads;
-    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < total_chunks;
-         i += static_cast<int64_t>(gridDim.x) * kThreads) {
-        const int64_t token = i / per_token;
-        const int32_t rem = static_cast<int32_t>(i - token * per_token);
-        const int32_t h = rem / chunks_per_row;
-        const int32_t c = rem - h * chunks_per_row;
-        // the token's rows and its slot are independent loads: all three are in flight together
-        // (the empty asm uses the rows here, so they are not moved behind the slot test)
-        const u32x4 kv = *reinterpret_cast<const u32x4 *>(key + token * key_stride_b + h * row_bytes + c * 16);
-        const u32x4 vv = *reinterpret_cast<const u32x4 *>(value + token * value_stride_b + h * row_bytes + c * 16);
-        const int64_t slot = slots[token];
-        asm volatile("" ::"v"(kv), "v"(vv));
-        if (slot < 0 || slot >= num_slots) continue;  // padding, or a slot outside the pool
-        const int64_t blk = block_shift >= 0 ? slot >> block_shift : slot / block_size;
-        const int64_t off = slot - blk * block_size;
-        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_bytes + c * 16;
-        *reinterpret_cast<u32x4 *>(k_cache + dst) = kv;
-        *reinterpret_cast<u32x4 *>(v_cache + dst) = vv;
+    const I per_token = static_cast<I>(chunks_per_row) * num_kv_heads;
+    const I stride = static_cast<I>(gridDim.x) * kThreads;
+    for (I i0 = static_cast<I>(blockIdx.x) * kThreads + threadIdx.x; i0 < total_chunks; i0 += stride * kWriteUnroll) {
+        u32x4 kv[kWriteUnroll], vv[kWriteUnroll];
+        int64_t slot[kWriteUnroll];
+        int32_t h[kWriteUnroll], c[kWriteUnroll];
+#pragma unroll
+        for (int u = 0; u < kWriteUnroll; ++u) {
+            const I i = i0 + u * stride;
+            slot[u] = -1;
+            if (i < total_chunks) {
+                const I token = i / per_token;
+                const int32_t rem = static_cast<int32_t>(i - token * per_token);
+                h[u] = rem / chunks_per_row;
+                c[u] = rem - h[u] * chunks_per_row;
+                kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    key + static_cast<int64_t>(token) * key_stride_b + h[u] * row_bytes + c[u] * 16));
+                vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    value + static_cast<int64_t>(token) * value_stride_b + h[u] * row_bytes + c[u] * 16));
+                slot[u] = slots[token];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kWriteUnroll; ++u) {
+            // padding, a slot outside the pool, or a chunk past the end
+            if (slot[u] < 0 || slot[u] >= num_slots) continue;
+            const int64_t blk = block_shift >= 0 ? slot[u] >> block_shift : slot[u] / block_size;
+            const int64_t off = slot[u] - blk * block_size;
+            const int64_t dst = ((blk * num_kv_heads + h[u]) * block_size + off) * row_bytes + c[u] * 16;
+            *reinterpret_cast<u32x4 *>(k_cache + dst) = kv[u];
+            *reinterpret_cast<u32x4 *>(v_cache + dst) = vv[u];
+        }
     }
 }
 
 constexpr int kMaxLayers = 16;
-constexpr int kMaxPairs = 64;
+constexpr int kMaxPairs = 448;  // per launch: the pairs travel in the kernel arguments (about 3.8 KiB)
+constexpr int kCopyUnroll = 4;
 
 struct CopyArgs {
     char *cache[2 * kMaxLayers];  // K of layer l at 2l, V at 2l+1
@@ -53,13 +71,27 @@ struct CopyArgs {
 };
 
 // grid = (slices, pairs, 2 * layers): workgroup (x, p, c) copies slice x of pair p in cache c.
+// kCopyUnroll independent 16-byte loads per thread are issued before their stores: source and
+// destination may alias as far as the compiler knows, so a plain loop would wait for each load
+// before the next, one load in flight per thread. Loads and stores are non-temporal: nothing
+// in the launch reads a byte twice.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const CopyArgs a) {
     char *base = a.cache[blockIdx.z];
     const char *src = base + a.src[blockIdx.y] * a.block_bytes;
     char *dst = base + a.dst[blockIdx.y] * a.block_bytes;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads * 16;
     for (int64_t off = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 16; off < a.block_bytes;
-         off += static_cast<int64_t>(gridDim.x) * kThreads * 16)
-        *reinterpret_cast<u32x4 *>(dst + off) = *reinterpret_cast<const u32x4 *>(src + off);
+         off += step * kCopyUnroll) {
+        u32x4 x[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            if (off + u * step < a.block_bytes)
+                x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + off + u * step));
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u)
+            if (off + u * step < a.block_bytes)
+                __builtin_nontemporal_store(x[u], reinterpret_cast<u32x4 *>(dst + off + u * step));
+    }
 }
 
 constexpr int kSwapCaches = 8;
@@ -209,13 +241,20 @@ extern "C" int pkv_reshape_and_cache(const void *key, const void *value, int64_t
     }
     const int32_t cpr = static_cast<int32_t>(row_bytes / 16);
     const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * cpr;
-    const int64_t want = ceil_div(total, kThreads);
+    const int64_t want = ceil_div(total, static_cast<int64_t>(kThreads) * kWriteUnroll);
     const unsigned grid = static_cast<unsigned>(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const char *>(key), static_cast<const char *>(value), key_stride * eb,
-                       value_stride * eb, static_cast<char *>(k_cache), static_cast<char *>(v_cache),
-                       num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size,
-                       (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1);
+    const int32_t shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(block_size) : -1;
+    // 32-bit chunk indices while every index the grid forms stays below 2^31
+    if (total + static_cast<int64_t>(grid) * kThreads * kWriteUnroll < (int64_t(1) << 31))
+        hipLaunchKernelGGL(reshape_and_cache_kernel<int32_t>, dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const char *>(key), static_cast<const char *>(value), key_stride * eb,
+                           value_stride * eb, static_cast<char *>(k_cache), static_cast<char *>(v_cache),
+                           num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size, shift);
+    else
+        hipLaunchKernelGGL(reshape_and_cache_kernel<int64_t>, dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const char *>(key), static_cast<const char *>(value), key_stride * eb,
+                           value_stride * eb, static_cast<char *>(k_cache), static_cast<char *>(v_cache),
+                           num_blocks * block_size, slot_mapping, total, cpr, num_kv_heads, block_size, shift);
     return hip_status(hipGetLastError(), "pkv_reshape_and_cache launch");
 }
 
