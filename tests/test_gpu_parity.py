@@ -278,6 +278,25 @@ def test_copy_blocks_multilayer():
         assert np.array_equal(v.cpu().numpy().view(np.uint16), vh.view(np.uint16))
 
 
+
+def test_copy_blocks_many_pairs():
+    """More pairs than one launch takes (448 travel in the kernel arguments): 1,000 pairs over two
+    layers, byte-identical to the oracle's copies."""
+    rng = np.random.default_rng(23)
+    L, N, hkv, B, d = 2, 2400, 2, 16, 64
+    ks = [torch.from_numpy(synth.normal(rng, (N, hkv, B, d), 1.0, "f16")).cuda() for _ in range(L)]
+    vs = [torch.from_numpy(synth.normal(rng, (N, hkv, B, d), 1.0, "f16")).cuda() for _ in range(L)]
+    perm = rng.permutation(N).astype(np.int32)
+    pairs = np.stack([rng.choice(perm[:1200], 1000), perm[1200:2200]], axis=1).astype(np.int32)
+    host = [(k.cpu().numpy(), v.cpu().numpy()) for k, v in zip(ks, vs)]
+    kernels.copy_blocks(ks, vs, pairs)
+    torch.cuda.synchronize()
+    for (kh, vh), k, v in zip(host, ks, vs):
+        kh, vh = kh.copy(), vh.copy()
+        oracle.copy_blocks(kh, vh, pairs)
+        assert np.array_equal(k.cpu().numpy().view(np.uint16), kh.view(np.uint16))
+        assert np.array_equal(v.cpu().numpy().view(np.uint16), vh.view(np.uint16))
+
 # ---------------------------------------------------------------- copy-on-write sampling, step by step
 
 @pytest.mark.parametrize("full", [False, pytest.param(True, marks=pytest.mark.full)])
